@@ -1,0 +1,63 @@
+"""Plausible mistakes planted in a copy of the oracle (on the CPU) must each
+fail at least one pin.  The product oracle is untouched; each mutant is a
+textual edit of its C source compiled to a temporary library."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from refs import brute_force
+from varlen_attention_serving_amd import workloads as W
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ua_oracle.c")
+
+MUTANTS = {
+    "drop_scale": ("double x = p->scale * dot;", "double x = dot;"),
+    "alibi_sign": ("x += (double)slopes[head] * (double)(k - ctx);",
+                   "x -= (double)slopes[head] * (double)(k - ctx);"),
+    "alibi_offset_q_abs_sinks": ("(double)(k - ctx);", "(double)(k - q_abs);"),
+    "window_off_by_one": ("k < q_abs - p->window + 1 - UAO_WINDOW_EXTRA_KEY",
+                          "k < q_abs - p->window - UAO_WINDOW_EXTRA_KEY"),
+    "causal_off_by_one": ("if (p->causal && k > q_abs)", "if (p->causal && k >= q_abs)"),
+    "gqa_modulo": ("const int hk = head / g;", "const int hk = head % p->num_kv_heads;"),
+    "sink_not_in_z": ("double z = p->use_sinks ? exp(sink - m) : 0.0;", "double z = 0.0;"),
+    "softcap_unscaled": ("x = p->softcap * tanh(x / p->softcap);", "x = tanh(x);"),
+    "slot_from_wrong_block": ("int64_t slot = k % p->block_size;\n        int64_t k_off",
+                              "int64_t slot = (k + 1) % p->block_size;\n        int64_t k_off"),
+    "v_scale_dropped": ("out[e] += w * uao_load_kv(v_cache, v_off + e, p->kv_dtype, p->v_scale);",
+                        "out[e] += w * uao_load_kv(v_cache, v_off + e, p->kv_dtype, 1.0);"),
+    "ctx_ignored": ("const int64_t q_abs = ctx + i;", "const int64_t q_abs = i;"),
+}
+
+# Cases drawn from the pinned workloads: brute force is the independent check.
+CASES = [
+    dict(),
+    dict(softcap=2.0, use_alibi=True, window=9, use_sinks=True),
+    dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True, use_sinks=True, window=11),
+    dict(softcap=0.5),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o",
+                           str(so), str(mpath), "-lm"])
+    monkeypatch.setattr(oracle, "_lib", oracle.open_library(str(so)))
+    caught = False
+    for i, flags in enumerate(CASES):
+        w = W.random_small(500 + i, num_seqs=4, max_q=20, max_k=70, num_q_heads=4,
+                           num_kv_heads=2, head_dim=32, block_size=8, **flags)
+        o = oracle.attention(w)
+        ob, _ = brute_force(w)
+        if np.isnan(o).any() or np.max(np.abs(o - ob)) > 1e-9:
+            caught = True
+            break
+    assert caught, f"mutant {name} passed every pin"

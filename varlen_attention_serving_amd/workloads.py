@@ -1,0 +1,317 @@
+"""Seeded synthetic inputs for unified paged attention.
+
+This module only draws and stores inputs: sequence lengths, a randomly permuted
+paged KV pool with its block table, Q/K/V values and the per-head ALiBi slopes
+and sink logits.  It holds none of the attention arithmetic, so both the HIP
+path and the fp64 oracle can consume the same bytes.
+
+Layouts follow the unified paged attention page ("Unified paged attention on
+gfx950, from the math up", section 0 Notation): Q and O are packed varlen
+[total_q, H_q, d]; the K and V caches are [num_blocks, block_size, H_k, d];
+the block table maps a sequence's logical block to a physical block;
+``cu_seqlens_q`` packs the ragged query rows; ``seq_lens`` holds S_k per
+sequence (query rows are the last ``q_len`` key positions, ctx = S_k - q_len).
+
+Recipe (same for every workload):
+  * RNG is ``numpy.random.default_rng(seed)``; draw order is lengths ->
+    physical permutation -> Q -> K -> V -> sinks (slopes are deterministic).
+  * Values are N(0, 1) float32, rounded to nearest-even into the storage type
+    (bf16 / fp16); fp8 K/V are e4m3fn codes of x / scale with a per-tensor
+    scale = amax / 448.
+  * The pool holds sum(ceil(S_k / b)) used blocks plus max(16, 1%) slack
+    blocks, in a random physical order.  Unused blocks and the tail slots of
+    each sequence's last block are filled with NaN; unused block-table
+    entries are -1.  A correct kernel never lets those reach O.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+# Storage-type codes shared with the C boundary (plain integers, no arithmetic).
+DT_BF16, DT_F16, DT_FP8_E4M3 = 0, 1, 2
+DTYPE_NAMES = {DT_BF16: "bf16", DT_F16: "f16", DT_FP8_E4M3: "fp8_e4m3"}
+
+_NAN_BITS = {DT_BF16: 0x7FC0, DT_F16: 0x7E00, DT_FP8_E4M3: 0x7F}
+_CHUNK = 1 << 24  # elements per RNG draw, bounds peak host memory
+
+
+@dataclasses.dataclass
+class Workload:
+    """One batch of paged attention inputs (host copies, raw storage bits)."""
+
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q_dtype: int
+    kv_dtype: int
+    causal: bool
+    softcap: float           # 0 = off
+    window: int              # 0 = off; otherwise keep the last `window` keys
+    use_alibi: bool
+    use_sinks: bool
+    scale: float
+    q_lens: np.ndarray       # int32 [N]
+    seq_lens: np.ndarray     # int32 [N]   (S_k)
+    cu_seqlens_q: np.ndarray  # int32 [N+1]
+    block_table: np.ndarray  # int32 [N, max_blocks_per_seq], -1 where unused
+    num_blocks: int
+    q: np.ndarray            # uint16 [T_q, H_q, d] (bf16 / fp16 bits)
+    k_cache: np.ndarray      # uint16 or uint8 [num_blocks, b, H_k, d]
+    v_cache: np.ndarray
+    alibi_slopes: Optional[np.ndarray]  # float32 [H_q] or None
+    sinks: Optional[np.ndarray]         # float32 [H_q] or None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q_lens.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(self.q_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(self.seq_lens.max()) if self.num_seqs else 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def token_seq(self) -> np.ndarray:
+        """Sequence index of each packed query token."""
+        return np.repeat(np.arange(self.num_seqs, dtype=np.int64), self.q_lens)
+
+
+# ----------------------------------------------------------------------------
+# storage-type rounding (input preparation only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3fn codes (nearest-even) via torch's float8 cast."""
+    import torch
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _store(x: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == DT_BF16:
+        return f32_to_bf16_bits(x)
+    if dtype == DT_F16:
+        return f32_to_f16_bits(x)
+    raise ValueError(dtype)
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def _normal_stored(rng, shape, dtype) -> np.ndarray:
+    """N(0,1) drawn chunk by chunk straight into the 16-bit storage type."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = _store(rng.standard_normal(e - s, dtype=np.float32), dtype)
+    return out.reshape(shape)
+
+
+def _amax(x: np.ndarray) -> float:
+    flat = x.reshape(-1)
+    m = 0.0
+    for s in range(0, flat.size, _CHUNK):
+        m = max(m, float(np.abs(flat[s:s + _CHUNK]).max()))
+    return m
+
+
+def alibi_slopes(num_q_heads: int) -> np.ndarray:
+    """Geometric ALiBi slopes 2^(-8 h / H_q) for h = 1 .. H_q."""
+    h = np.arange(1, num_q_heads + 1, dtype=np.float64)
+    return np.exp2(-8.0 * h / num_q_heads).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# generic builder
+# ----------------------------------------------------------------------------
+
+def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_heads: int,
+          head_dim: int, block_size: int, q_dtype: int = DT_BF16, kv_dtype: int = DT_BF16,
+          causal: bool = True, softcap: float = 0.0, window: int = 0, use_alibi: bool = False,
+          use_sinks: bool = False, scale: Optional[float] = None, num_blocks: Optional[int] = None,
+          rng: Optional[np.random.Generator] = None, poison: bool = True,
+          table_slack_cols: int = 0) -> Workload:
+    """Draw one workload.  ``q_lens``/``seq_lens`` are already drawn by the caller
+    (from ``rng`` when random) so the lengths come first in the draw order."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    if q_lens.shape != seq_lens.shape:
+        raise ValueError("q_lens and seq_lens differ in length")
+    if np.any(q_lens > seq_lens) or np.any(q_lens < 0):
+        raise ValueError("need 0 <= q_len <= S_k")
+    n = q_lens.shape[0]
+    b = block_size
+    nb_seq = (seq_lens.astype(np.int64) + b - 1) // b
+    used = int(nb_seq.sum())
+    if num_blocks is None:
+        num_blocks = used + max(16, (used + 99) // 100)
+    if num_blocks < used:
+        raise ValueError("pool smaller than the blocks in use")
+    max_blocks = int(nb_seq.max()) + table_slack_cols if n else 1
+    max_blocks = max(max_blocks, 1)
+
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    block_table = np.full((n, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for s in range(n):
+        k = int(nb_seq[s])
+        block_table[s, :k] = perm[off:off + k]
+        off += k
+
+    cu = np.zeros(n + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    t_q = int(cu[-1])
+
+    q = _normal_stored(rng, (t_q, num_q_heads, head_dim), q_dtype)
+    cache_shape = (num_blocks, b, num_kv_heads, head_dim)
+    k_scale = v_scale = 1.0
+    if kv_dtype == DT_FP8_E4M3:
+        kf = _normal(rng, cache_shape)
+        vf = _normal(rng, cache_shape)
+        # per-tensor scales: amax over the pool, kept exactly representable in f32
+        k_scale = float(np.float32(_amax(kf) / 448.0))
+        v_scale = float(np.float32(_amax(vf) / 448.0))
+        k_cache = f32_to_e4m3_codes(kf / np.float32(k_scale))
+        del kf
+        v_cache = f32_to_e4m3_codes(vf / np.float32(v_scale))
+        del vf
+    else:
+        k_cache = _normal_stored(rng, cache_shape, kv_dtype)
+        v_cache = _normal_stored(rng, cache_shape, kv_dtype)
+
+    slopes = alibi_slopes(num_q_heads) if use_alibi else None
+    sinks = rng.standard_normal(num_q_heads, dtype=np.float32) if use_sinks else None
+
+    if poison:
+        nan = _NAN_BITS[kv_dtype]
+        in_use = np.zeros(num_blocks, dtype=bool)
+        for s in range(n):
+            k = int(nb_seq[s])
+            in_use[block_table[s, :k]] = True
+            tail = int(seq_lens[s]) - (k - 1) * b if k else b
+            if k and tail < b:
+                last = block_table[s, k - 1]
+                k_cache[last, tail:] = nan
+                v_cache[last, tail:] = nan
+        k_cache[~in_use] = nan
+        v_cache[~in_use] = nan
+
+    return Workload(
+        name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        block_size=b, q_dtype=q_dtype, kv_dtype=kv_dtype, causal=causal, softcap=float(softcap),
+        window=int(window), use_alibi=use_alibi, use_sinks=use_sinks,
+        scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
+        q_lens=q_lens, seq_lens=seq_lens, cu_seqlens_q=cu, block_table=block_table,
+        num_blocks=num_blocks, q=q, k_cache=k_cache, v_cache=v_cache, alibi_slopes=slopes,
+        sinks=sinks, k_scale=k_scale, v_scale=v_scale)
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+
+def tiny_varlen(seed: int = 1) -> Workload:
+    """4 sequences, q_lens {1,1,3,8}, S_k {17,40,64,100}, H_q=4, H_k=2, d=64,
+    b=16, a 32-block pool, bf16, causal."""
+    return build("tiny_varlen", seed, [1, 1, 3, 8], [17, 40, 64, 100], num_q_heads=4,
+                 num_kv_heads=2, head_dim=64, block_size=16, num_blocks=32)
+
+
+def decode_batch(seed: int = 2) -> Workload:
+    """64 decode sequences, S_k ~ U{512..8192}, H_q=32, H_k=8, d=128, b=16, bf16, causal."""
+    rng = np.random.default_rng(seed)
+    sk = rng.integers(512, 8192, size=64, endpoint=True)
+    return build("decode_batch", seed, np.ones(64, np.int32), sk, num_q_heads=32,
+                 num_kv_heads=8, head_dim=128, block_size=16, rng=rng)
+
+
+def chunked_prefill_mix(seed: int = 3) -> Workload:
+    """32 decode sequences (S_k ~ U{1024..8192}) then 4 chunks of 512 queries with
+    ctx ~ U{2048..6144}; H_q=32, H_k=8, d=128, b=32, bf16, causal, softcap 50,
+    window 4096."""
+    rng = np.random.default_rng(seed)
+    dec = rng.integers(1024, 8192, size=32, endpoint=True)
+    ctx = rng.integers(2048, 6144, size=4, endpoint=True)
+    q_lens = np.concatenate([np.ones(32, np.int64), np.full(4, 512)])
+    sk = np.concatenate([dec, ctx + 512])
+    return build("chunked_prefill_mix", seed, q_lens, sk, num_q_heads=32, num_kv_heads=8,
+                 head_dim=128, block_size=32, softcap=50.0, window=4096, rng=rng)
+
+
+def long_prefill(seed: int = 4) -> Workload:
+    """1 sequence S_q=S_k=8192 plus 4 of 2048; H_q=128, H_k=8, d=128, b=64, bf16, causal."""
+    lens = [8192, 2048, 2048, 2048, 2048]
+    return build("long_prefill", seed, lens, lens, num_q_heads=128, num_kv_heads=8,
+                 head_dim=128, block_size=64)
+
+
+def variant_mix(seed: int = 5) -> Workload:
+    """128 decode sequences (S_k ~ U{1024..16384}) plus 2 prefill sequences of 1024;
+    H_q=16, H_k=2, d=256, b=64; fp16 Q, fp8-e4m3 K/V with per-tensor scales;
+    ALiBi, per-head sinks, window 2048, causal, tau = 1/16."""
+    rng = np.random.default_rng(seed)
+    dec = rng.integers(1024, 16384, size=128, endpoint=True)
+    q_lens = np.concatenate([np.ones(128, np.int64), np.full(2, 1024)])
+    sk = np.concatenate([dec, np.full(2, 1024)])
+    return build("variant_mix", seed, q_lens, sk, num_q_heads=16, num_kv_heads=2, head_dim=256,
+                 block_size=64, q_dtype=DT_F16, kv_dtype=DT_FP8_E4M3, window=2048,
+                 use_alibi=True, use_sinks=True, scale=1.0 / 16.0, rng=rng)
+
+
+NAMED = {
+    "tiny_varlen": tiny_varlen,
+    "decode_batch": decode_batch,
+    "chunked_prefill_mix": chunked_prefill_mix,
+    "long_prefill": long_prefill,
+    "variant_mix": variant_mix,
+}
+
+
+def random_small(seed: int, *, num_seqs: int = 3, max_q: int = 40, max_k: int = 130,
+                 num_q_heads: int = 4, num_kv_heads: int = 2, head_dim: int = 64,
+                 block_size: int = 16, **kw) -> Workload:
+    """A small ragged batch (oracle finishes in well under a second)."""
+    rng = np.random.default_rng(seed)
+    sk = rng.integers(1, max_k, size=num_seqs, endpoint=True)
+    ql = np.minimum(sk, rng.integers(1, max_q, size=num_seqs, endpoint=True))
+    return build(f"random_small_{seed}", seed, ql, sk, num_q_heads=num_q_heads,
+                 num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                 rng=rng, **kw)
