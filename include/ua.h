@@ -1,0 +1,172 @@
+/*
+ * ua.h -- unified paged attention forward pass for MI355X (gfx950).
+ *
+ * One kernel family computes, for every packed query row of a varlen batch,
+ *
+ *     O_i = sum_j softmax_j( bias/mask( tau * Q_i K_j^T ) ) V_j
+ *
+ * over a block-table-paged KV cache with grouped-query heads, serving decode
+ * (S_q = 1), chunked prefill (1 < S_q < S_k) and prefill (S_q = S_k) alike.
+ * The operation and its bias/mask order (scale, softcap, ALiBi, causal,
+ * sliding window, sinks) are the specification of "Unified paged attention on
+ * gfx950, from the math up", section 1; the layouts are its section 0; the
+ * two kernel strategies (a 2D query-tile kernel and a 3D split-KV kernel with a
+ * log-sum-exp reduce) and the shape rule between them are its sections 4-6.
+ *
+ * Conventions for every entry point:
+ *  - Plain C ABI; no C++ exceptions cross it.  Every call returns a status
+ *    code; on failure ua_last_error() returns a thread-local message.
+ *  - "device" pointers are HIP device memory owned by the caller; the library
+ *    never allocates, frees or synchronises on the run path.
+ *  - Streams are passed as `void*` holding a hipStream_t (NULL = the default
+ *    stream).
+ */
+#ifndef UA_H
+#define UA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ua_status {
+    UA_OK = 0,
+    UA_ERR_INVALID_ARG = 1,  /* a descriptor field or run argument is out of range */
+    UA_ERR_UNSUPPORTED = 2,  /* valid, but no kernel is built for it (e.g. head_dim 96) */
+    UA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than ua_workspace_size() */
+    UA_ERR_HIP = 4           /* a HIP launch reported an error */
+} ua_status_t;
+
+/* Storage types.  Q and O share q_dtype; K and V share kv_dtype, which is
+ * q_dtype or UA_DTYPE_FP8_E4M3 (OCP e4m3fn codes times a per-tensor scale;
+ * "Unified paged attention on gfx950", section 7.3). */
+typedef enum ua_dtype {
+    UA_DTYPE_BF16 = 0,
+    UA_DTYPE_F16 = 1,
+    UA_DTYPE_FP8_E4M3 = 2
+} ua_dtype_t;
+
+/* Problem flags (section 1 of the unified page, one flag per bias/mask). */
+enum {
+    UA_FLAG_CAUSAL = 1u << 0,   /* mask keys k > q_abs (q_abs = ctx + local row) */
+    UA_FLAG_SOFTCAP = 1u << 1,  /* s <- c tanh(s / c) after the scale */
+    UA_FLAG_ALIBI = 1u << 2,    /* s += slope_h (k - ctx) */
+    UA_FLAG_WINDOW = 1u << 3,   /* keep the last `window` keys: q_abs - W < k <= q_abs */
+    UA_FLAG_SINKS = 1u << 4,    /* per-head logit joins the softmax with no value row */
+    UA_FLAG_FORCE_2D = 1u << 8, /* testing/benchmarking: bypass the shape rule */
+    UA_FLAG_FORCE_3D = 1u << 9
+};
+
+/* Problem description: everything that fixes the kernel and the plan bounds.
+ * All fields are host values; creating a problem touches no device. */
+typedef struct ua_problem_desc {
+    int32_t num_q_heads;         /* H_q > 0 */
+    int32_t num_kv_heads;        /* H_k > 0, H_q % H_k == 0, g = H_q / H_k <= 128 */
+    int32_t head_dim;            /* d in {64, 128, 256} */
+    int32_t block_size;          /* b in {16, 32, 64} (KV positions per physical block) */
+    int32_t q_dtype;             /* UA_DTYPE_BF16 or UA_DTYPE_F16 */
+    int32_t kv_dtype;            /* q_dtype or UA_DTYPE_FP8_E4M3 */
+    uint32_t flags;              /* UA_FLAG_* */
+    float scale;                 /* tau > 0 (usually 1/sqrt(d)) */
+    float softcap;               /* c > 0 when UA_FLAG_SOFTCAP */
+    int32_t window;              /* W > 0 when UA_FLAG_WINDOW */
+    float k_scale;               /* fp8 only: real K = decode(code) * k_scale (> 0) */
+    float v_scale;               /* fp8 only: real V = decode(code) * v_scale (> 0) */
+    int64_t num_blocks;          /* physical blocks in each of the K and V pools */
+    int32_t max_num_seqs;        /* upper bound for ua_run_args.num_seqs */
+    int32_t max_blocks_per_seq;  /* upper bound for ua_run_args.block_table_stride use */
+    int64_t max_total_q;         /* upper bound for ua_run_args.total_q */
+    int32_t max_seqlen_k;        /* upper bound for any S_k (sizes the split workspace) */
+} ua_problem_desc_t;
+
+typedef struct ua_problem* ua_problem_t;
+
+/* Arguments of one forward pass.
+ *  q            device, [total_q, H_q, d] in q_dtype; token stride q_stride_tok
+ *               elements, heads and d contiguous.
+ *  k_cache,
+ *  v_cache      device, [num_blocks, b, H_k, d] in kv_dtype, contiguous.
+ *  o            device, [total_q, H_q, d] in q_dtype; token stride o_stride_tok.
+ *               Must not alias q or the caches.
+ *  block_table  device int32 [num_seqs, block_table_stride]; entry [s][j] is the
+ *               physical block of sequence s's logical block j.  Entries past
+ *               ceil(S_k / b) are never read.
+ *  seq_lens     device int32 [num_seqs]: S_k per sequence (cached + new tokens).
+ *  cu_seqlens_q device int32 [num_seqs + 1]: prefix sums of the query lengths;
+ *               sequence s owns tokens [cu[s], cu[s+1]) which are its last
+ *               q_len key positions (ctx = S_k - q_len).
+ *  alibi_slopes device f32 [H_q] when UA_FLAG_ALIBI, else NULL.
+ *  sinks        device f32 [H_q] (natural-log logits) when UA_FLAG_SINKS, else NULL.
+ *  workspace    device, >= ua_workspace_size() bytes, 256-byte aligned; used
+ *               only by the split-KV path (may be NULL if that size is 0).
+ *  num_seqs, total_q, max_seqlen_q, max_seqlen_k are host copies of the
+ *  batch's shape (no device reads on the host side).
+ * Device metadata is trusted: 0 <= q_len <= S_k <= max_seqlen_k, and used
+ * block-table entries lie in [0, num_blocks). */
+typedef struct ua_run_args {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    void* o;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* cu_seqlens_q;
+    const float* alibi_slopes;
+    const float* sinks;
+    void* workspace;
+    size_t workspace_bytes;
+    int32_t num_seqs;
+    int32_t max_seqlen_q;
+    int64_t total_q;
+    int32_t max_seqlen_k;
+    int32_t block_table_stride;
+    int64_t q_stride_tok;
+    int64_t o_stride_tok;
+} ua_run_args_t;
+
+/* Which kernel strategy a run takes (section 6 of the unified page). */
+typedef struct ua_plan_info {
+    int32_t path;            /* 2 = 2D query-tile kernel, 3 = 3D split-KV + reduce */
+    int32_t block_m;         /* query rows (position, head) per workgroup */
+    int32_t block_q;         /* query positions per workgroup */
+    int32_t tile_n;          /* keys per KV tile */
+    int32_t waves;           /* wave64s per workgroup */
+    int32_t num_segments;    /* split-KV segments per q-block (1 on the 2D path) */
+    int32_t tiles_per_segment;
+    int32_t grid[3];         /* launch grid of the attention kernel */
+    int32_t use_i64_kv;      /* 1 when the KV pool exceeds 2^31 bytes */
+} ua_plan_info_t;
+
+/* Validate a description and build a problem handle (host only; no device
+ * access).  Returns UA_ERR_INVALID_ARG / UA_ERR_UNSUPPORTED with a message. */
+ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out);
+
+/* Bytes of device workspace ua_run needs at the description's maxima (the
+ * split-KV partials of section 5 of the unified page: fp32 o, m and l per
+ * query row, head and segment).  0 for a NULL handle. */
+size_t ua_workspace_size(ua_problem_t problem);
+
+/* The plan ua_run would launch for these host-side shape values (host only). */
+ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_q,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k, ua_plan_info_t* info);
+
+/* Enqueue one forward pass on `stream` (asynchronous; nothing is read back to
+ * the host).  Validation errors return before anything is enqueued. */
+ua_status_t ua_run(ua_problem_t problem, const ua_run_args_t* args, void* stream);
+
+/* Release a handle (NULL is ignored). */
+void ua_destroy_problem(ua_problem_t problem);
+
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char* ua_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* ua_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UA_H */

@@ -1,0 +1,206 @@
+"""The C boundary without a GPU: the library loads, exports every function
+include/ua.h declares, rejects invalid descriptors and run arguments with a
+status code and a message (before touching a device), sizes its workspace and
+plans each named workload on the path the shape rule gives."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from varlen_attention_serving_amd import binding as B
+from varlen_attention_serving_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ua.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(ua_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_all_exported():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_empty_error():
+    assert re.match(r"^\d+\.\d+\.\d+$", B.ua_version())
+    h = B.ua_create_problem(_desc())
+    assert B.ua_last_error() == ""
+    B.ua_destroy_problem(h)
+    B.ua_destroy_problem(None)
+
+
+def _desc(**kw):
+    d = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+             q_dtype=B.UA_DTYPE_BF16, kv_dtype=B.UA_DTYPE_BF16, flags=B.UA_FLAG_CAUSAL,
+             scale=0.088, softcap=0.0, window=0, k_scale=1.0, v_scale=1.0, num_blocks=100,
+             max_num_seqs=8, max_blocks_per_seq=64, max_total_q=512, max_seqlen_k=1024)
+    d.update(kw)
+    return B.ua_problem_desc_t(**d)
+
+
+BAD_DESCS = [
+    (dict(num_q_heads=0), B.UA_ERR_INVALID_ARG, "head counts"),
+    (dict(num_q_heads=6, num_kv_heads=4), B.UA_ERR_INVALID_ARG, "multiple"),
+    (dict(num_q_heads=256, num_kv_heads=1), B.UA_ERR_UNSUPPORTED, "GQA group"),
+    (dict(head_dim=96), B.UA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=-1), B.UA_ERR_INVALID_ARG, "head_dim"),
+    (dict(block_size=24), B.UA_ERR_INVALID_ARG, "block_size"),
+    (dict(q_dtype=B.UA_DTYPE_FP8_E4M3), B.UA_ERR_UNSUPPORTED, "q_dtype"),
+    (dict(kv_dtype=B.UA_DTYPE_F16), B.UA_ERR_UNSUPPORTED, "kv_dtype"),
+    (dict(flags=1 << 20), B.UA_ERR_INVALID_ARG, "unknown flag"),
+    (dict(flags=B.UA_FLAG_FORCE_2D | B.UA_FLAG_FORCE_3D), B.UA_ERR_INVALID_ARG, "exclusive"),
+    (dict(scale=0.0), B.UA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), B.UA_ERR_INVALID_ARG, "scale"),
+    (dict(flags=B.UA_FLAG_SOFTCAP, softcap=0.0), B.UA_ERR_INVALID_ARG, "softcap"),
+    (dict(flags=B.UA_FLAG_WINDOW, window=0), B.UA_ERR_INVALID_ARG, "window"),
+    (dict(kv_dtype=B.UA_DTYPE_FP8_E4M3, k_scale=0.0), B.UA_ERR_INVALID_ARG, "k_scale"),
+    (dict(num_blocks=0), B.UA_ERR_INVALID_ARG, "num_blocks"),
+    (dict(max_seqlen_k=2048, max_blocks_per_seq=64), B.UA_ERR_INVALID_ARG, "max_blocks_per_seq"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BAD_DESCS)))
+def test_invalid_descriptors_are_rejected(i):
+    kw, status, text = BAD_DESCS[i]
+    with pytest.raises(B.UaError) as e:
+        B.ua_create_problem(_desc(**kw))
+    assert e.value.status == status
+    assert text in B.ua_last_error()
+
+
+def test_null_pointers_are_rejected():
+    h = ctypes.c_void_p()
+    assert B.lib.ua_create_problem(None, ctypes.byref(h)) == B.UA_ERR_INVALID_ARG
+    assert B.lib.ua_run(None, None, None) == B.UA_ERR_INVALID_ARG
+    assert B.lib.ua_query_plan(None, 0, 0, 0, 0, None) == B.UA_ERR_INVALID_ARG
+
+
+def _args(**kw):
+    fake = 1 << 20  # aligned non-null placeholder; validation fails before any use
+    a = dict(q=fake, k_cache=fake, v_cache=fake, o=fake, block_table=fake, seq_lens=fake,
+             cu_seqlens_q=fake, alibi_slopes=None, sinks=None, workspace=None, workspace_bytes=0,
+             num_seqs=2, max_seqlen_q=4, total_q=8, max_seqlen_k=512, block_table_stride=64,
+             q_stride_tok=1024, o_stride_tok=1024)
+    a.update(kw)
+    return B.ua_run_args_t(**a)
+
+
+BAD_ARGS = [
+    (dict(num_seqs=9), B.UA_ERR_INVALID_ARG, "num_seqs"),
+    (dict(total_q=513), B.UA_ERR_INVALID_ARG, "total_q"),
+    (dict(max_seqlen_k=1025), B.UA_ERR_INVALID_ARG, "max_seqlen_k"),
+    (dict(max_seqlen_q=600), B.UA_ERR_INVALID_ARG, "max_seqlen_q"),
+    (dict(q_stride_tok=1000), B.UA_ERR_INVALID_ARG, "strides"),
+    (dict(o_stride_tok=1028), B.UA_ERR_INVALID_ARG, "multiples of 8"),
+    (dict(block_table_stride=8), B.UA_ERR_INVALID_ARG, "block_table_stride"),
+    (dict(q=None), B.UA_ERR_INVALID_ARG, "null required"),
+    (dict(cu_seqlens_q=None), B.UA_ERR_INVALID_ARG, "null required"),
+    (dict(o=(1 << 20) + 2), B.UA_ERR_INVALID_ARG, "aligned"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BAD_ARGS)))
+def test_invalid_run_arguments_are_rejected(i):
+    kw, status, text = BAD_ARGS[i]
+    h = B.ua_create_problem(_desc())
+    try:
+        with pytest.raises(B.UaError) as e:
+            B.ua_run(h, _args(**kw), None)
+        assert e.value.status == status
+        assert text in B.ua_last_error()
+    finally:
+        B.ua_destroy_problem(h)
+
+
+def test_flagged_inputs_need_their_pointers():
+    for flag, text in ((B.UA_FLAG_ALIBI, "alibi_slopes"), (B.UA_FLAG_SINKS, "sinks")):
+        h = B.ua_create_problem(_desc(flags=B.UA_FLAG_CAUSAL | flag))
+        with pytest.raises(B.UaError, match=text):
+            B.ua_run(h, _args(), None)
+        B.ua_destroy_problem(h)
+
+
+def test_split_path_needs_workspace():
+    h = B.ua_create_problem(_desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_FORCE_3D))
+    assert B.ua_workspace_size(h) > 0
+    with pytest.raises(B.UaError) as e:
+        B.ua_run(h, _args(), None)
+    assert e.value.status == B.UA_ERR_WORKSPACE
+    B.ua_destroy_problem(h)
+
+
+def test_empty_batch_returns_ok_without_launch():
+    h = B.ua_create_problem(_desc())
+    B.ua_run(h, _args(num_seqs=0, total_q=0, max_seqlen_q=0, q=None), None)
+    B.ua_destroy_problem(h)
+
+
+def _named_plan(name, extra=0):
+    sp = W.named_spec(name)
+    kw = sp["kw"]
+    ql = np.asarray(sp["q_lens"])
+    sk = np.asarray(sp["seq_lens"])
+    b = kw["block_size"]
+    flags = B.UA_FLAG_CAUSAL | extra
+    if kw.get("softcap", 0) > 0:
+        flags |= B.UA_FLAG_SOFTCAP
+    if kw.get("window", 0) > 0:
+        flags |= B.UA_FLAG_WINDOW
+    if kw.get("use_alibi"):
+        flags |= B.UA_FLAG_ALIBI
+    if kw.get("use_sinks"):
+        flags |= B.UA_FLAG_SINKS
+    d = B.ua_problem_desc_t(
+        num_q_heads=kw["num_q_heads"], num_kv_heads=kw["num_kv_heads"], head_dim=kw["head_dim"],
+        block_size=b, q_dtype=kw.get("q_dtype", 0), kv_dtype=kw.get("kv_dtype", 0), flags=flags,
+        scale=kw.get("scale", kw["head_dim"] ** -0.5), softcap=kw.get("softcap", 0.0),
+        window=kw.get("window", 0), k_scale=0.01, v_scale=0.01,
+        num_blocks=int(((sk + b - 1) // b).sum()) + 16, max_num_seqs=len(ql),
+        max_blocks_per_seq=int((sk.max() + b - 1) // b), max_total_q=int(ql.sum()),
+        max_seqlen_k=int(sk.max()))
+    h = B.ua_create_problem(d)
+    try:
+        return B.ua_query_plan(h, len(ql), int(ql.sum()), int(ql.max()), int(sk.max())), \
+            B.ua_workspace_size(h)
+    finally:
+        B.ua_destroy_problem(h)
+
+
+@pytest.mark.parametrize("name,path", [("tiny_varlen", 2), ("decode_batch", 3),
+                                       ("chunked_prefill_mix", 2), ("long_prefill", 2),
+                                       ("variant_mix", 2)])
+def test_shape_rule_picks_the_pages_path(name, path):
+    plan, ws = _named_plan(name)
+    assert plan.path == path
+    if path == 3:
+        assert plan.tiles_per_segment >= 4
+        assert plan.num_segments * plan.tiles_per_segment * plan.tile_n >= 8138
+        assert list(plan.grid)[1:] == [8, plan.num_segments]
+    else:
+        assert plan.num_segments == 1 and plan.grid[2] == 1
+    assert ws < (2 << 30) + 1
+
+
+def test_forced_paths_and_geometry():
+    plan, _ = _named_plan("long_prefill", B.UA_FLAG_FORCE_3D)
+    assert plan.path == 3 and plan.waves == 4 and plan.block_q == 8
+    plan, _ = _named_plan("decode_batch", B.UA_FLAG_FORCE_2D)
+    assert plan.path == 2 and plan.waves == 1 and plan.block_m == 32
+
+
+def test_i64_addressing_reported_above_2gib():
+    small, _ = _named_plan("decode_batch")
+    assert small.use_i64_kv == 0
+    h = B.ua_create_problem(_desc(num_blocks=600_000))  # 600K * 16 * 2 * 128 * 2 B > 2^31
+    p = B.ua_query_plan(h, 2, 8, 4, 512)
+    assert p.use_i64_kv == 1
+    B.ua_destroy_problem(h)

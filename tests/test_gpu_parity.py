@@ -1,0 +1,180 @@
+"""HIP path vs the fp64 oracle, through the C boundary, on an MI355X.
+
+Small batches are compared element by element (several tiles, ragged tails,
+every flag, both strategies forced); the five named workloads at full size are
+compared on sampled rows the oracle computes one by one, in the launch
+configuration the benchmark times.  The bar is max-abs <= 2e-2 and relative
+RMS <= 5e-3 against the oracle, and bitwise agreement where the result must
+not depend on physical placement or on the run."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import compare, compare_rows, run_hip, sample_rows, say
+from varlen_attention_serving_amd import binding as B
+from varlen_attention_serving_amd import device as D
+from varlen_attention_serving_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+FORCE = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _full_check(w, force="auto", what=None):
+    what = what or f"{w.name}/{force}"
+    say(f"[gpu] {what}: T_q={w.total_q} H={w.num_q_heads}/{w.num_kv_heads} d={w.head_dim} "
+        f"b={w.block_size}")
+    o, plan = run_hip(w, FORCE[force])
+    say(f"  plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
+        f"segments={plan.num_segments} tps={plan.tiles_per_segment} grid={list(plan.grid)}")
+    if force == "2d":
+        assert plan.path == 2
+    if force == "3d":
+        assert plan.path == 3
+    compare(o, oracle.attention(w), what)
+    return o, plan
+
+
+@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+def test_tiny_varlen(force):
+    _full_check(W.tiny_varlen(), force)
+
+
+SMALL_CASES = [
+    ("plain", dict()),
+    ("noncausal", dict(causal=False)),
+    ("softcap", dict(softcap=3.0)),
+    ("alibi", dict(use_alibi=True)),
+    ("window", dict(window=37)),
+    ("window_noncausal", dict(window=29, causal=False)),
+    ("sinks", dict(use_sinks=True)),
+    ("all_flags", dict(softcap=5.0, use_alibi=True, window=45, use_sinks=True)),
+    ("f16", dict(q_dtype=W.DT_F16, kv_dtype=W.DT_F16)),
+    ("fp8_bf16q", dict(kv_dtype=W.DT_FP8_E4M3)),
+    ("fp8_f16q_all", dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True,
+                          use_sinks=True, window=50, softcap=20.0)),
+]
+SHAPES = [
+    # (H_q, H_k, d, b): GQA groups 1, 2, 4, 8, 16; head dims 64/128/256; blocks 8..64
+    (4, 2, 64, 16),
+    (8, 2, 128, 32),
+    (16, 2, 256, 64),
+    (32, 2, 128, 16),
+    (6, 6, 64, 8),
+]
+
+
+@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_small_batches(case, shape, force):
+    name, flags = SMALL_CASES[case]
+    hq, hk, d, b = SHAPES[shape]
+    w = W.random_small(1000 + 17 * case + shape, num_seqs=5, max_q=70, max_k=300,
+                       num_q_heads=hq, num_kv_heads=hk, head_dim=d, block_size=b, **flags)
+    _full_check(w, force, f"{name}/{SHAPES[shape]}/{force}")
+
+
+@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+def test_decode_only_batch(force):
+    """Single-query rows, S_k from 1 up to several tiles (the decode geometry)."""
+    rng = np.random.default_rng(7)
+    sk = np.concatenate([[1, 2, 31, 32, 33, 64, 65], rng.integers(1, 700, size=20)])
+    w = W.build("decode_small", 7, np.ones(sk.size), sk, num_q_heads=32, num_kv_heads=8,
+                head_dim=128, block_size=16, rng=rng)
+    _full_check(w, force)
+
+
+@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+def test_prefill_ragged(force):
+    """Self-attention prefill with lengths that are not tile multiples."""
+    lens = [1, 63, 64, 65, 127, 200]
+    w = W.build("prefill_ragged", 8, lens, lens, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                block_size=32)
+    _full_check(w, force)
+
+
+def test_empty_and_zero_length_sequences():
+    """Sequences with q_len 0 own no q-block; the others are unaffected."""
+    w = W.build("with_empty", 9, [0, 3, 0, 1, 5], [10, 40, 7, 1, 90], num_q_heads=8,
+                num_kv_heads=4, head_dim=64, block_size=16)
+    _full_check(w)
+
+
+def test_empty_batch_is_a_no_op():
+    w = W.tiny_varlen()
+    batch = D.DeviceBatch(w)
+    ua = D.UnifiedAttention(D.problem_desc(w))
+    args = batch.run_args(ua.workspace)
+    args.num_seqs = 0
+    args.total_q = 0
+    args.max_seqlen_q = 0
+    B.ua_run(ua.handle, args, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(batch.o).item() == 0
+
+
+def test_block_table_permutation_is_bitwise_invariant():
+    w = W.random_small(44, num_seqs=4, max_q=40, max_k=400, num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16)
+    for force in ("2d", "3d"):
+        base, _ = run_hip(w, FORCE[force])
+        rng = np.random.default_rng(5)
+        perm = rng.permutation(w.num_blocks)
+        w2 = W.Workload(**{**w.__dict__})
+        w2.k_cache = np.empty_like(w.k_cache)
+        w2.v_cache = np.empty_like(w.v_cache)
+        w2.k_cache[perm] = w.k_cache
+        w2.v_cache[perm] = w.v_cache
+        w2.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)],
+                                  -1).astype(np.int32)
+        moved, _ = run_hip(w2, FORCE[force])
+        say(f"[gpu] permutation invariance ({force})")
+        assert np.array_equal(base, moved)
+
+
+def test_run_to_run_determinism():
+    w = W.random_small(45, num_seqs=4, max_q=60, max_k=500, num_q_heads=16, num_kv_heads=4,
+                       head_dim=128, block_size=32, use_sinks=True)
+    for force in ("2d", "3d"):
+        a, _ = run_hip(w, FORCE[force])
+        b, _ = run_hip(w, FORCE[force])
+        assert np.array_equal(a, b)
+
+
+def test_nan_poison_in_unused_blocks_and_tails_never_reaches_output():
+    w = W.random_small(46, num_seqs=6, max_q=30, max_k=250, num_q_heads=8, num_kv_heads=2,
+                       head_dim=64, block_size=64)
+    assert np.isnan(oracle.attention(w)).sum() == 0
+    for force in ("2d", "3d"):
+        o, _ = run_hip(w, FORCE[force])
+        assert not np.isnan(o).any()
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads at full size (sampled rows)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["decode_batch", "chunked_prefill_mix", "long_prefill",
+                                  "variant_mix"])
+def test_named_workload_full_size(name):
+    say(f"[gpu] {name}: generating")
+    w = W.NAMED[name]()
+    batch = D.DeviceBatch(w)
+    ua = D.UnifiedAttention(D.problem_desc(w))
+    o, plan = run_hip(w, batch=batch, ua=ua)
+    say(f"  plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
+        f"segments={plan.num_segments} tps={plan.tiles_per_segment} grid={list(plan.grid)}")
+    rows = sample_rows(w, n_random=384)
+    compare_rows(o, w, rows, f"{name} ({rows.size} sampled rows)")
+    # a second run in the same configuration is bitwise identical
+    o2, _ = run_hip(w, batch=batch, ua=ua)
+    assert np.array_equal(o, o2)

@@ -1,0 +1,56 @@
+// ua_internal.h -- parameters shared by the host plan and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Everything a kernel of the family reads, passed by value at launch.
+struct UaKernelParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* cu_q;
+    const float* slopes;      // ALiBi slopes (natural units) or null
+    const float* sinks;       // sink logits (natural units) or null
+    float* ws_o;              // split partials: un-normalised o  [rows, NS, D]
+    float* ws_m;              //                 running max (log2 units) [rows, NS]
+    float* ws_l;              //                 denominator           [rows, NS]
+    int64_t q_stride_tok;     // elements
+    int64_t o_stride_tok;     // elements
+    int64_t kv_slot_stride;   // elements between consecutive slots = H_k * D
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;            // g = H_q / H_k
+    int32_t block_size_log2;
+    int32_t bt_stride;
+    int32_t block_q;          // query positions per q-block
+    int32_t rows_used;        // block_q * g  (<= rows per workgroup)
+    int32_t tile_n;           // keys per KV tile of the attention kernel
+    int32_t tiles_per_seg;    // split path: KV tiles per segment
+    int32_t num_segments;     // split path: segments per q-block (workspace stride)
+    uint32_t flags;           // UA_FLAG_* bits
+    int32_t window;
+    float qk_scale_log2;      // tau * k_scale * log2(e)
+    float softcap_in;         // tau * k_scale / c
+    float softcap_out;        // c * log2(e)
+    float out_scale;          // v_scale for fp8 V, else 1
+};
+
+struct UaLaunch {
+    int path;        // 2 or 3
+    int waves;       // 1 or 4
+    int tile_n;
+    int head_dim;
+    int q_dtype;     // UA_DTYPE_BF16 / UA_DTYPE_F16
+    int kv_fp8;      // 1 when K/V are e4m3fn
+    unsigned grid[3];
+    int64_t reduce_rows;  // split path: total_q * H_q
+};
+
+hipError_t ua_launch_d64(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
+hipError_t ua_launch_d128(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
+hipError_t ua_launch_d256(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);

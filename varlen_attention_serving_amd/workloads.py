@@ -17,7 +17,9 @@ Recipe (same for every workload):
     physical permutation -> Q -> K -> V -> sinks (slopes are deterministic).
   * Values are N(0, 1) float32, rounded to nearest-even into the storage type
     (bf16 / fp16); fp8 K/V are e4m3fn codes of x / scale with a per-tensor
-    scale = amax / 448.
+    scale = amax / 448 (rounded to fp16 first, then to e4m3fn).  Large
+    tensors are drawn in 16M-value chunks, chunk i from child i of one seed
+    drawn from the workload's generator (thread-count independent).
   * The pool holds sum(ceil(S_k / b)) used blocks plus max(16, 1%) slack
     blocks, in a random physical order.  Unused blocks and the tail slots of
     each sequence's last block are filled with NaN; unused block-table
@@ -25,8 +27,10 @@ Recipe (same for every workload):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -99,21 +103,31 @@ class Workload:
 # ----------------------------------------------------------------------------
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bfloat16 (nearest, ties to even); finite inputs only."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
+    """Round float32 to bfloat16 (nearest, ties to even) via torch's cast."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
+_E4M3_LUT = None
+
+
 def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
-    """float32 -> OCP e4m3fn codes (nearest-even) via torch's float8 cast."""
-    import torch
-    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
-    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    """float32 -> OCP e4m3fn codes: round to fp16 first (nearest-even), then to
+    the nearest e4m3fn value (nearest-even, saturating at +-448) through a
+    65536-entry table built once with torch's float8 cast."""
+    global _E4M3_LUT
+    if _E4M3_LUT is None:
+        import torch
+        halves = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float32)
+        halves = np.clip(np.nan_to_num(halves, nan=0.0), -448.0, 448.0)
+        _E4M3_LUT = torch.from_numpy(halves).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    h = np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0).astype(np.float16)
+    return _E4M3_LUT[h.view(np.uint16)]
 
 
 def _store(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -124,12 +138,31 @@ def _store(x: np.ndarray, dtype: int) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _parallel_normal(rng: np.random.Generator, n: int, out: np.ndarray, convert) -> None:
+    """Fill out[0:n] with convert(N(0,1) float32 draws).  Chunk i draws from its
+    own child of one seed taken from ``rng``, so the values do not depend on
+    the number of threads."""
+    chunks = (n + _CHUNK - 1) // _CHUNK
+    seeds = np.random.SeedSequence(int(rng.integers(0, 2**63))).spawn(max(chunks, 1))
+
+    def work(i):
+        s = i * _CHUNK
+        e = min(n, s + _CHUNK)
+        x = np.random.default_rng(seeds[i]).standard_normal(e - s, dtype=np.float32)
+        out[s:e] = convert(x)
+
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(chunks)))
+
+
 def _normal(rng: np.random.Generator, shape) -> np.ndarray:
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    _parallel_normal(rng, n, out, lambda x: x)
     return out.reshape(shape)
 
 
@@ -137,18 +170,28 @@ def _normal_stored(rng, shape, dtype) -> np.ndarray:
     """N(0,1) drawn chunk by chunk straight into the 16-bit storage type."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = _store(rng.standard_normal(e - s, dtype=np.float32), dtype)
+    _parallel_normal(rng, n, out, lambda x: _store(x, dtype))
     return out.reshape(shape)
 
 
 def _amax(x: np.ndarray) -> float:
     flat = x.reshape(-1)
-    m = 0.0
-    for s in range(0, flat.size, _CHUNK):
-        m = max(m, float(np.abs(flat[s:s + _CHUNK]).max()))
-    return m
+    spans = [(s, min(flat.size, s + _CHUNK)) for s in range(0, flat.size, _CHUNK)]
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        return max([0.0] + list(ex.map(lambda se: float(np.abs(flat[se[0]:se[1]]).max()), spans)))
+
+
+def _encode_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    flat = x.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint8)
+    inv = np.float32(scale)
+
+    def work(se):
+        out[se[0]:se[1]] = f32_to_e4m3_codes(flat[se[0]:se[1]] / inv)
+
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, [(s, min(flat.size, s + _CHUNK)) for s in range(0, flat.size, _CHUNK)]))
+    return out.reshape(x.shape)
 
 
 def alibi_slopes(num_q_heads: int) -> np.ndarray:
@@ -209,9 +252,9 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
         # per-tensor scales: amax over the pool, kept exactly representable in f32
         k_scale = float(np.float32(_amax(kf) / 448.0))
         v_scale = float(np.float32(_amax(vf) / 448.0))
-        k_cache = f32_to_e4m3_codes(kf / np.float32(k_scale))
+        k_cache = _encode_e4m3(kf, k_scale)
         del kf
-        v_cache = f32_to_e4m3_codes(vf / np.float32(v_scale))
+        v_cache = _encode_e4m3(vf, v_scale)
         del vf
     else:
         k_cache = _normal_stored(rng, cache_shape, kv_dtype)
@@ -248,52 +291,95 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
 # the five named workloads
 # ----------------------------------------------------------------------------
 
-def tiny_varlen(seed: int = 1) -> Workload:
+def _spec_tiny_varlen(seed):
     """4 sequences, q_lens {1,1,3,8}, S_k {17,40,64,100}, H_q=4, H_k=2, d=64,
     b=16, a 32-block pool, bf16, causal."""
-    return build("tiny_varlen", seed, [1, 1, 3, 8], [17, 40, 64, 100], num_q_heads=4,
-                 num_kv_heads=2, head_dim=64, block_size=16, num_blocks=32)
+    return dict(q_lens=[1, 1, 3, 8], seq_lens=[17, 40, 64, 100], rng=None,
+                kw=dict(num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                        num_blocks=32))
 
 
-def decode_batch(seed: int = 2) -> Workload:
+def _spec_decode_batch(seed):
     """64 decode sequences, S_k ~ U{512..8192}, H_q=32, H_k=8, d=128, b=16, bf16, causal."""
     rng = np.random.default_rng(seed)
     sk = rng.integers(512, 8192, size=64, endpoint=True)
-    return build("decode_batch", seed, np.ones(64, np.int32), sk, num_q_heads=32,
-                 num_kv_heads=8, head_dim=128, block_size=16, rng=rng)
+    return dict(q_lens=np.ones(64, np.int32), seq_lens=sk, rng=rng,
+                kw=dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16))
 
 
-def chunked_prefill_mix(seed: int = 3) -> Workload:
+def _spec_chunked_prefill_mix(seed):
     """32 decode sequences (S_k ~ U{1024..8192}) then 4 chunks of 512 queries with
     ctx ~ U{2048..6144}; H_q=32, H_k=8, d=128, b=32, bf16, causal, softcap 50,
     window 4096."""
     rng = np.random.default_rng(seed)
     dec = rng.integers(1024, 8192, size=32, endpoint=True)
     ctx = rng.integers(2048, 6144, size=4, endpoint=True)
-    q_lens = np.concatenate([np.ones(32, np.int64), np.full(4, 512)])
-    sk = np.concatenate([dec, ctx + 512])
-    return build("chunked_prefill_mix", seed, q_lens, sk, num_q_heads=32, num_kv_heads=8,
-                 head_dim=128, block_size=32, softcap=50.0, window=4096, rng=rng)
+    return dict(q_lens=np.concatenate([np.ones(32, np.int64), np.full(4, 512)]),
+                seq_lens=np.concatenate([dec, ctx + 512]), rng=rng,
+                kw=dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=32,
+                        softcap=50.0, window=4096))
 
 
-def long_prefill(seed: int = 4) -> Workload:
+def _spec_long_prefill(seed):
     """1 sequence S_q=S_k=8192 plus 4 of 2048; H_q=128, H_k=8, d=128, b=64, bf16, causal."""
     lens = [8192, 2048, 2048, 2048, 2048]
-    return build("long_prefill", seed, lens, lens, num_q_heads=128, num_kv_heads=8,
-                 head_dim=128, block_size=64)
+    return dict(q_lens=lens, seq_lens=lens, rng=None,
+                kw=dict(num_q_heads=128, num_kv_heads=8, head_dim=128, block_size=64))
 
 
-def variant_mix(seed: int = 5) -> Workload:
+def _spec_variant_mix(seed):
     """128 decode sequences (S_k ~ U{1024..16384}) plus 2 prefill sequences of 1024;
     H_q=16, H_k=2, d=256, b=64; fp16 Q, fp8-e4m3 K/V with per-tensor scales;
     ALiBi, per-head sinks, window 2048, causal, tau = 1/16."""
     rng = np.random.default_rng(seed)
     dec = rng.integers(1024, 16384, size=128, endpoint=True)
-    q_lens = np.concatenate([np.ones(128, np.int64), np.full(2, 1024)])
-    sk = np.concatenate([dec, np.full(2, 1024)])
-    return build("variant_mix", seed, q_lens, sk, num_q_heads=16, num_kv_heads=2, head_dim=256,
-                 block_size=64, q_dtype=DT_F16, kv_dtype=DT_FP8_E4M3, window=2048,
-                 use_alibi=True, use_sinks=True, scale=1.0 / 16.0, rng=rng)
+    return dict(q_lens=np.concatenate([np.ones(128, np.int64), np.full(2, 1024)]),
+                seq_lens=np.concatenate([dec, np.full(2, 1024)]), rng=rng,
+                kw=dict(num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=64,
+                        q_dtype=DT_F16, kv_dtype=DT_FP8_E4M3, window=2048, use_alibi=True,
+                        use_sinks=True, scale=1.0 / 16.0))
+
+
+NAMED_SPECS = {
+    "tiny_varlen": (1, _spec_tiny_varlen),
+    "decode_batch": (2, _spec_decode_batch),
+    "chunked_prefill_mix": (3, _spec_chunked_prefill_mix),
+    "long_prefill": (4, _spec_long_prefill),
+    "variant_mix": (5, _spec_variant_mix),
+}
+
+
+def named_spec(name: str, seed: Optional[int] = None) -> dict:
+    """Lengths and parameters of a named workload, without drawing any values."""
+    default_seed, fn = NAMED_SPECS[name]
+    return fn(default_seed if seed is None else seed)
+
+
+def named(name: str, seed: Optional[int] = None) -> Workload:
+    default_seed, fn = NAMED_SPECS[name]
+    seed = default_seed if seed is None else seed
+    sp = fn(seed)
+    return build(name, seed, sp["q_lens"], sp["seq_lens"], rng=sp["rng"], **sp["kw"])
+
+
+def tiny_varlen(seed: int = 1) -> Workload:
+    return named("tiny_varlen", seed)
+
+
+def decode_batch(seed: int = 2) -> Workload:
+    return named("decode_batch", seed)
+
+
+def chunked_prefill_mix(seed: int = 3) -> Workload:
+    return named("chunked_prefill_mix", seed)
+
+
+def long_prefill(seed: int = 4) -> Workload:
+    return named("long_prefill", seed)
+
+
+def variant_mix(seed: int = 5) -> Workload:
+    return named("variant_mix", seed)
 
 
 NAMED = {
