@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the unified paged attention forward pass on one MI355X.
+
+A step is one ``ua_run`` over one batch of synthetic inputs already resident in
+HBM: the host plan, then the attention kernel (and, on the split-KV path, the
+log-sum-exp reduce).  The default workload is the decode batch (64 sequences,
+S_k ~ U{512..8192}, H_q/H_k = 32/8, d = 128, b = 16, bf16, causal), which is
+HBM-bound: its value is algorithmic GB/s.  MFMA-bound workloads report
+TFLOP/s.  One JSON line is printed.
+
+Algorithmic work (counted from the realised lengths):
+  bytes = K+V of every key visible to at least one row, once per (sequence,
+          KV head) + Q + O + the block-table entries of visited blocks +
+          sequence metadata (+ slopes / sinks);
+  flops = 4 d per visible (query row, key, query head) triple.
+The roofline object prices the dominant (attention) kernel alone: its bytes
+(the above without O when a reduce kernel writes O) or flops per launch over
+its mean duration, from HIP events recorded around it on its own stream.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 MFMA
+METRIC = "paged-attn TFLOPS (prefill) & HBM GB/s (decode) on 1 MI355X, % of roofline"
+CSRC = os.path.join(ROOT, "varlen_attention_serving_amd", "csrc")
+
+
+def algorithmic_work(w):
+    """Visible (row, key) pairs and visited keys per sequence, from lengths."""
+    pairs = 0
+    visited = np.zeros(w.num_seqs, dtype=np.int64)
+    blocks = 0
+    for s in range(w.num_seqs):
+        ql, sk = int(w.q_lens[s]), int(w.seq_lens[s])
+        if ql == 0:
+            continue
+        ctx = sk - ql
+        q_abs = ctx + np.arange(ql, dtype=np.int64)
+        kmax = np.minimum(q_abs, sk - 1) if w.causal else np.full(ql, sk - 1)
+        kmin = np.maximum(q_abs - w.window + 1, 0) if w.window > 0 else np.zeros(ql, np.int64)
+        pairs += int((kmax - kmin + 1).sum())
+        lo, hi = int(kmin[0]), int(kmax[-1])
+        visited[s] = hi - lo + 1
+        blocks += hi // w.block_size - lo // w.block_size + 1
+    esz_kv = 1 if w.kv_dtype == 2 else 2
+    kv_bytes = int(visited.sum()) * w.num_kv_heads * w.head_dim * esz_kv * 2
+    q_bytes = w.total_q * w.num_q_heads * w.head_dim * 2
+    meta = blocks * 4 + w.num_seqs * 4 + (w.num_seqs + 1) * 4
+    meta += (w.num_q_heads * 4 if w.use_alibi else 0) + (w.num_q_heads * 4 if w.use_sinks else 0)
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    dense_flops = 4 * w.head_dim * w.num_q_heads * int(
+        (w.q_lens.astype(np.int64) * w.seq_lens.astype(np.int64)).sum())
+    return dict(kv_bytes=kv_bytes, q_bytes=q_bytes, o_bytes=q_bytes, meta_bytes=meta,
+                bytes=kv_bytes + 2 * q_bytes + meta, flops=flops, dense_flops=dense_flops,
+                pairs=pairs, visited_keys=int(visited.sum()))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, path_id):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    f = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("path") != path_id:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, untuned, on whole sequences drawn in a seeded order until
+    about `budget_s` of wall time; reported in the metric's unit."""
+    import oracle
+    threads = oracle.default_threads()
+    order = np.random.default_rng(123).permutation(w.num_seqs)
+    done_bytes = done_flops = 0
+    seqs = 0
+    t_total = 0.0
+    for s in order:
+        lo, hi = int(w.cu_seqlens_q[s]), int(w.cu_seqlens_q[s + 1])
+        if hi == lo:
+            continue
+        rows = np.arange(lo * w.num_q_heads, hi * w.num_q_heads, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.rows(w, rows, nthreads=threads)
+        t_total += time.perf_counter() - t0
+        sub = _subset(w, s)
+        a = algorithmic_work(sub)
+        done_bytes += a["bytes"]
+        done_flops += a["flops"]
+        seqs += 1
+        if t_total >= budget_s:
+            break
+    return dict(seconds=t_total, bytes=done_bytes, flops=done_flops, seqs=seqs, cores=threads)
+
+
+def _subset(w, s):
+    import copy
+    sub = copy.copy(w)
+    sub.q_lens = w.q_lens[s:s + 1]
+    sub.seq_lens = w.seq_lens[s:s + 1]
+    sub.cu_seqlens_q = np.array([0, int(w.q_lens[s])], dtype=np.int32)
+    return sub
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_batch",
+                    choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
+                             "variant_mix", "tiny_varlen"])
+    ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-time budget of the oracle CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from varlen_attention_serving_amd import binding as B
+    from varlen_attention_serving_amd import device as D
+    from varlen_attention_serving_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = W.named(args.workload)
+    extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[args.force]
+    batch = D.DeviceBatch(w)
+    ua = D.UnifiedAttention(D.problem_desc(w, extra))
+    plan = ua.plan(w)
+    work = algorithmic_work(w)
+    t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    stream = torch.cuda.current_stream()
+    handle = ua.handle
+    run_args = batch.run_args(ua.workspace)
+
+    print(f"[bench] plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
+          f"segments={plan.num_segments} grid={list(plan.grid)}; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        B.ua_run(handle, run_args, stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    # events around the kernels of every timed step (created by one record first)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for trio in evs:
+        for e in trio:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for j in range(3):
+            run_args.timing_events[j] = evs[i][j].cuda_event
+        B.ua_run(handle, run_args, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    attn_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]))
+    step_gpu_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][2]) for i in range(args.steps)]))
+
+    if bound == "hbm":
+        value = work["bytes"] / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        kernel_units = work["bytes"] - (work["o_bytes"] if plan.path == 3 else 0)
+        achieved = kernel_units / (attn_ms * 1e-3) / 1e9
+        peak = HBM_PEAK_GBS
+        r_unit = "GB/s"
+    else:
+        value = work["flops"] / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        kernel_units = work["flops"]
+        achieved = kernel_units / (attn_ms * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS
+        r_unit = "TFLOP/s"
+    traffic = load_traffic(args.workload, plan.path)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        c = cpu_baseline(w, args.cpu_seconds)
+        cpu_value = (c["bytes"] / c["seconds"] / 1e9) if bound == "hbm" else \
+            (c["flops"] / c["seconds"] / 1e12)
+        cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": c["cores"], "kind": "oracle",
+               "sample": f"{c['seqs']} of {w.num_seqs} sequences (all their rows and heads), "
+                         f"{c['seconds']:.1f} s of fp64 oracle time on {c['cores']} threads"}
+
+    dtype = {0: "bf16", 1: "f16"}[w.q_dtype] + ("+fp8kv" if w.kv_dtype == 2 else "")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": w.num_seqs, "total_q": w.total_q, "max_seqlen_k": w.max_seqlen_k,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size,
+            "path": {2: "2d", 3: "3d-split-kv"}[plan.path], "segments": plan.num_segments,
+            "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+            "dense_equivalent_flops": work["dense_flops"],
+            "gpu_ms_per_step_events": round(step_gpu_ms, 5),
+            "attention_kernel_ms": round(attn_ms, 5),
+            "roofline_frac_whole_step": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
+        },
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": r_unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

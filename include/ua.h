@@ -103,6 +103,10 @@ typedef struct ua_problem* ua_problem_t;
  *               only by the split-KV path (may be NULL if that size is 0).
  *  num_seqs, total_q, max_seqlen_q, max_seqlen_k are host copies of the
  *  batch's shape (no device reads on the host side).
+ *  timing_events  optional hipEvent_t handles (NULL to skip each): [0] is
+ *               recorded on the stream before the attention kernel, [1] after
+ *               it (before the split-KV reduce, if any), [2] after the last
+ *               kernel, so a caller can time the kernels one by one.
  * Device metadata is trusted: 0 <= q_len <= S_k <= max_seqlen_k, and used
  * block-table entries lie in [0, num_blocks). */
 typedef struct ua_run_args {
@@ -124,6 +128,7 @@ typedef struct ua_run_args {
     int32_t block_table_stride;
     int64_t q_stride_tok;
     int64_t o_stride_tok;
+    void* timing_events[3];
 } ua_run_args_t;
 
 /* Which kernel strategy a run takes (section 6 of the unified page). */

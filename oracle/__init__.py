@@ -84,7 +84,12 @@ def lib():
 
 
 def default_threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)))
+    """Host threads for the oracle: the affinity set, capped by OMP_NUM_THREADS."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _ptr(a: Optional[np.ndarray]):

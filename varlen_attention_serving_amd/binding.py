@@ -10,6 +10,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# Device memory and streams come from torch, whose wheel carries its own HIP
+# runtime.  Load it first so libua.so binds to that same runtime instead of
+# pulling a second copy into the process.
+import torch  # noqa: F401
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libua.so")
 
@@ -74,6 +79,7 @@ class ua_run_args_t(ctypes.Structure):
         ("block_table_stride", ctypes.c_int32),
         ("q_stride_tok", ctypes.c_int64),
         ("o_stride_tok", ctypes.c_int64),
+        ("timing_events", ctypes.c_void_p * 3),
     ]
 
 

@@ -313,6 +313,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     l.kv_fp8 = p->fp8;
     for (int i = 0; i < 3; ++i) l.grid[i] = pl.grid[i];
     l.reduce_rows = a->total_q * d.num_q_heads;
+    for (int i = 0; i < 3; ++i) l.events[i] = static_cast<hipEvent_t>(a->timing_events[i]);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

@@ -460,16 +460,22 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
 template <int D, int NW, int BN, typename QT, bool FP8>
 hipError_t launch_attn(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
     dim3 grid(l.grid[0], l.grid[1], l.grid[2]);
+    hipError_t e = hipSuccess;
+    if (l.events[0] && (e = hipEventRecord(l.events[0], st)) != hipSuccess) return e;
     if (l.path == 3) {
         hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true>), grid, dim3(NW * 64), 0, st, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
         const unsigned nb = (unsigned)((l.reduce_rows + 3) / 4);
         hipLaunchKernelGGL((ua_reduce_kernel<D, QT>), dim3(nb), dim3(256), 0, st, p, l.reduce_rows);
     } else {
         hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false>), grid, dim3(NW * 64), 0, st, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
     }
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (l.events[2] && (e = hipEventRecord(l.events[2], st)) != hipSuccess) return e;
+    return hipSuccess;
 }
 
 template <int D, typename QT, bool FP8>

@@ -49,6 +49,7 @@ struct UaLaunch {
     int kv_fp8;      // 1 when K/V are e4m3fn
     unsigned grid[3];
     int64_t reduce_rows;  // split path: total_q * H_q
+    hipEvent_t events[3]; // optional: before attention, between kernels, at the end
 };
 
 hipError_t ua_launch_d64(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
