@@ -131,6 +131,8 @@ def main():
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
                              "variant_mix", "tiny_varlen"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
+    ap.add_argument("--segment-tiles", type=int, default=0,
+                    help="split-KV segment length in KV tiles (0 = the plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -153,7 +155,7 @@ def main():
     w = W.named(args.workload)
     extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[args.force]
     batch = D.DeviceBatch(w)
-    ua = D.UnifiedAttention(D.problem_desc(w, extra))
+    ua = D.UnifiedAttention(D.problem_desc(w, extra, split_segment_tiles=args.segment_tiles))
     plan = ua.plan(w)
     work = algorithmic_work(w)
     t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)

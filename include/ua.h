@@ -79,6 +79,8 @@ typedef struct ua_problem_desc {
     int32_t max_blocks_per_seq;  /* upper bound for ua_run_args.block_table_stride use */
     int64_t max_total_q;         /* upper bound for ua_run_args.total_q */
     int32_t max_seqlen_k;        /* upper bound for any S_k (sizes the split workspace) */
+    int32_t split_segment_tiles; /* 0 = automatic; else KV tiles per split-KV segment
+                                    (>= 1; a tuning override of the plan) */
 } ua_problem_desc_t;
 
 typedef struct ua_problem* ua_problem_t;
@@ -142,6 +144,8 @@ typedef struct ua_plan_info {
     int32_t tiles_per_segment;
     int32_t grid[3];         /* launch grid of the attention kernel */
     int32_t use_i64_kv;      /* 1 when the KV pool exceeds 2^31 bytes */
+    int32_t stream_k;        /* 1 when the split path balances KV tiles over resident
+                                workers (decode-shaped batches), 0 for fixed segments */
 } ua_plan_info_t;
 
 /* Validate a description and build a problem handle (host only; no device

@@ -16,12 +16,13 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_hip(w, extra_flags=0, batch=None, ua=None, repeat=1):
+def run_hip(w, extra_flags=0, batch=None, ua=None, repeat=1, split_segment_tiles=0):
     """Run the HIP path on workload w; returns (O as float64 numpy, plan)."""
     if batch is None:
         batch = D.DeviceBatch(w)
     if ua is None:
-        ua = D.UnifiedAttention(D.problem_desc(w, extra_flags))
+        ua = D.UnifiedAttention(D.problem_desc(w, extra_flags,
+                                               split_segment_tiles=split_segment_tiles))
     plan = ua.plan(w)
     for _ in range(repeat):
         ua.run(batch)

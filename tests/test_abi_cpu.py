@@ -144,7 +144,7 @@ def test_empty_batch_returns_ok_without_launch():
     B.ua_destroy_problem(h)
 
 
-def _named_plan(name, extra=0):
+def _named_plan(name, extra=0, split_segment_tiles=0):
     sp = W.named_spec(name)
     kw = sp["kw"]
     ql = np.asarray(sp["q_lens"])
@@ -166,7 +166,7 @@ def _named_plan(name, extra=0):
         window=kw.get("window", 0), k_scale=0.01, v_scale=0.01,
         num_blocks=int(((sk + b - 1) // b).sum()) + 16, max_num_seqs=len(ql),
         max_blocks_per_seq=int((sk.max() + b - 1) // b), max_total_q=int(ql.sum()),
-        max_seqlen_k=int(sk.max()))
+        max_seqlen_k=int(sk.max()), split_segment_tiles=split_segment_tiles)
     h = B.ua_create_problem(d)
     try:
         return B.ua_query_plan(h, len(ql), int(ql.sum()), int(ql.max()), int(sk.max())), \
@@ -182,12 +182,21 @@ def test_shape_rule_picks_the_pages_path(name, path):
     plan, ws = _named_plan(name)
     assert plan.path == path
     if path == 3:
-        assert plan.tiles_per_segment >= 4
-        assert plan.num_segments * plan.tiles_per_segment * plan.tile_n >= 8138
-        assert list(plan.grid)[1:] == [8, plan.num_segments]
+        # decode-shaped: every sequence fits one q-block, so the split is stream-K
+        assert plan.stream_k == 1 and plan.waves == 1 and plan.tile_n == 32
     else:
+        assert plan.stream_k == 0
         assert plan.num_segments == 1 and plan.grid[2] == 1
     assert ws < (2 << 30) + 1
+
+
+def test_segment_override_selects_the_segmented_split():
+    plan, _ = _named_plan("decode_batch", split_segment_tiles=16)
+    assert plan.path == 3 and plan.stream_k == 0 and plan.tiles_per_segment == 16
+    assert plan.num_segments * 16 * plan.tile_n >= 8138
+    assert list(plan.grid)[1:] == [8, plan.num_segments]
+    with pytest.raises(B.UaError):
+        B.ua_create_problem(_desc(split_segment_tiles=-1))
 
 
 def test_forced_paths_and_geometry():

@@ -18,7 +18,9 @@ from varlen_attention_serving_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-FORCE = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}
+FORCE = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D,
+         "3d_seg": B.UA_FLAG_FORCE_3D}
+SEG_TILES = {"3d_seg": 2}  # a segment override selects the segmented split
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -32,13 +34,16 @@ def _full_check(w, force="auto", what=None):
     what = what or f"{w.name}/{force}"
     say(f"[gpu] {what}: T_q={w.total_q} H={w.num_q_heads}/{w.num_kv_heads} d={w.head_dim} "
         f"b={w.block_size}")
-    o, plan = run_hip(w, FORCE[force])
-    say(f"  plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
-        f"segments={plan.num_segments} tps={plan.tiles_per_segment} grid={list(plan.grid)}")
+    o, plan = run_hip(w, FORCE[force], split_segment_tiles=SEG_TILES.get(force, 0))
+    say(f"  plan path={plan.path} stream_k={plan.stream_k} waves={plan.waves} "
+        f"tile_n={plan.tile_n} segments={plan.num_segments} tps={plan.tiles_per_segment} "
+        f"grid={list(plan.grid)}")
     if force == "2d":
         assert plan.path == 2
-    if force == "3d":
+    if force in ("3d", "3d_seg"):
         assert plan.path == 3
+    if force == "3d_seg":
+        assert plan.stream_k == 0
     compare(o, oracle.attention(w), what)
     return o, plan
 
@@ -72,7 +77,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+@pytest.mark.parametrize("force", ["auto", "2d", "3d", "3d_seg"])
 @pytest.mark.parametrize("shape", range(len(SHAPES)))
 @pytest.mark.parametrize("case", range(len(SMALL_CASES)))
 def test_small_batches(case, shape, force):
@@ -83,7 +88,7 @@ def test_small_batches(case, shape, force):
     _full_check(w, force, f"{name}/{SHAPES[shape]}/{force}")
 
 
-@pytest.mark.parametrize("force", ["auto", "2d", "3d"])
+@pytest.mark.parametrize("force", ["auto", "2d", "3d", "3d_seg"])
 def test_decode_only_batch(force):
     """Single-query rows, S_k from 1 up to several tiles (the decode geometry)."""
     rng = np.random.default_rng(7)
@@ -91,6 +96,23 @@ def test_decode_only_batch(force):
     w = W.build("decode_small", 7, np.ones(sk.size), sk, num_q_heads=32, num_kv_heads=8,
                 head_dim=128, block_size=16, rng=rng)
     _full_check(w, force)
+
+
+@pytest.mark.parametrize("hk", [1, 2, 8])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_stream_k_ragged_decode(seed, hk):
+    """Decode-shaped batches with lengths from 1 to many tiles, empty
+    sequences in between and short multi-row chunks: the stream-K workers'
+    ranges start and end inside pairs, cross several pairs, or are empty."""
+    rng = np.random.default_rng(300 + seed)
+    n = [3, 40, 150][seed]
+    sk = rng.integers(1, [70, 3000, 1200][seed], size=n, endpoint=True)
+    ql = np.minimum(sk, rng.integers(0, 3, size=n, endpoint=True))  # 0..3 rows
+    w = W.build(f"sk_{seed}_{hk}", 300 + seed, ql, sk, num_q_heads=4 * hk, num_kv_heads=hk,
+                head_dim=128, block_size=16, rng=rng, use_sinks=seed == 1,
+                use_alibi=seed == 2, softcap=30.0 if seed == 2 else 0.0)
+    _, plan = _full_check(w, "3d")
+    assert plan.stream_k == 1
 
 
 @pytest.mark.parametrize("force", ["auto", "2d", "3d"])

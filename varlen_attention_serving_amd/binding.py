@@ -56,6 +56,7 @@ class ua_problem_desc_t(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_total_q", ctypes.c_int64),
         ("max_seqlen_k", ctypes.c_int32),
+        ("split_segment_tiles", ctypes.c_int32),
     ]
 
 
@@ -94,6 +95,7 @@ class ua_plan_info_t(ctypes.Structure):
         ("tiles_per_segment", ctypes.c_int32),
         ("grid", ctypes.c_int32 * 3),
         ("use_i64_kv", ctypes.c_int32),
+        ("stream_k", ctypes.c_int32),
     ]
 
 

@@ -54,13 +54,19 @@ struct ua_problem {
 
 namespace {
 
+int row_bytes(const ua_problem& P) { return (P.d.head_dim + 2) * 4; }
+
 struct Plan {
-    int path, waves, tile_n, block_m, block_q, num_segments, tiles_per_seg;
+    int path, waves, tile_n, block_m, block_q, num_segments, tiles_per_seg, stream_k;
     int64_t slots;
     unsigned grid[3];
 };
 
-int row_bytes(const ua_problem& P) { return (P.d.head_dim + 2) * 4; }
+// stream-K partial slots: one per (sequence, kv-head) pair plus one per worker
+size_t stream_k_bytes(const ua_problem& P, int64_t num_seqs, int rows_per_slot) {
+    return (size_t)(num_seqs * P.d.num_kv_heads + kMaxStreamKWorkers) * rows_per_slot *
+           (size_t)row_bytes(P);
+}
 
 ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, int32_t max_q,
                       int32_t max_k, Plan* out) {
@@ -88,6 +94,19 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         pl.grid[0] = d.num_kv_heads;
         pl.grid[1] = (unsigned)pl.slots;
         pl.grid[2] = 1;
+    } else if (small && d.split_segment_tiles == 0 &&
+               (int64_t)num_seqs * d.num_kv_heads * (cdiv(std::max(max_k, 1), kSkTile) + 1) <
+                   INT32_MAX) {
+        // every sequence's rows fit one q-block: balance KV tiles over workers
+        pl.path = 3;
+        pl.stream_k = 1;
+        pl.num_segments = 0;
+        pl.tiles_per_seg = 0;
+        pl.grid[0] = 0;  // resident worker count, fixed at launch
+        pl.grid[1] = 1;
+        pl.grid[2] = 1;
+        if (stream_k_bytes(P, num_seqs, pl.block_q * P.group) > P.ws_bytes)
+            return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
     } else {
         pl.path = 3;
         const int64_t max_tiles = std::max<int64_t>(1, cdiv(std::max(max_k, 1), pl.tile_n));
@@ -96,6 +115,7 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         const int64_t live_blocks = std::min<int64_t>(pl.slots, num_seqs + total_q / pl.block_q);
         const int64_t work = std::max<int64_t>(1, d.num_kv_heads * live_blocks * max_tiles / 2);
         int64_t tps = std::max<int64_t>(kMinTilesPerSegment, cdiv(work, kSplitTargetWorkgroups));
+        if (d.split_segment_tiles > 0) tps = d.split_segment_tiles;
         tps = std::min(tps, max_tiles);
         int64_t ns = cdiv(max_tiles, tps);
         const int64_t rows = std::max<int64_t>(1, total_q * d.num_q_heads);
@@ -166,6 +186,8 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     if (d.max_num_seqs < 0 || d.max_total_q < 0 || d.max_seqlen_k < 0 || d.max_blocks_per_seq < 0)
         return fail(UA_ERR_INVALID_ARG, "negative maxima");
     if (d.max_total_q > INT32_MAX) return fail(UA_ERR_UNSUPPORTED, "max_total_q exceeds 2^31");
+    if (d.split_segment_tiles < 0)
+        return fail(UA_ERR_INVALID_ARG, "split_segment_tiles must be >= 0");
     if ((int64_t)d.max_blocks_per_seq * d.block_size < d.max_seqlen_k)
         return fail(UA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size < max_seqlen_k");
 
@@ -180,10 +202,15 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     // then gets fewer, longer segments)
     const size_t rows = (size_t)std::max<int64_t>(1, d.max_total_q) * d.num_q_heads;
     const size_t per_seg = rows * (size_t)row_bytes(*P);
+    const int64_t min_tps = d.split_segment_tiles > 0
+                                ? std::min<int64_t>(d.split_segment_tiles, kMinTilesPerSegment)
+                                : kMinTilesPerSegment;
     const int64_t ns_max =
-        std::max<int64_t>(1, cdiv(cdiv(std::max(d.max_seqlen_k, 1), 32), kMinTilesPerSegment));
+        std::max<int64_t>(1, cdiv(cdiv(std::max(d.max_seqlen_k, 1), 32), min_tps));
     const int64_t ns_cap = std::max<int64_t>(1, (int64_t)(kWorkspaceCap / per_seg));
     P->ws_bytes = per_seg * (size_t)std::min(ns_max, ns_cap);
+    // the stream-K split (single-wave geometry, 32 rows per q-block)
+    P->ws_bytes = std::max(P->ws_bytes, stream_k_bytes(*P, std::max(d.max_num_seqs, 1), 32));
     *out = P;
     return UA_OK;
 }
@@ -212,6 +239,7 @@ ua_status_t ua_query_plan(ua_problem_t p, int32_t num_seqs, int64_t total_q, int
     info->tiles_per_segment = pl.tiles_per_seg;
     for (int i = 0; i < 3; ++i) info->grid[i] = (int32_t)pl.grid[i];
     const int esz = p->fp8 ? 1 : 2;
+    info->stream_k = pl.stream_k;
     info->use_i64_kv =
         (double)p->d.num_blocks * p->d.block_size * p->d.num_kv_heads * p->d.head_dim * esz >
         2147483648.0;
@@ -290,7 +318,21 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     kp.softcap_out = (d.flags & UA_FLAG_SOFTCAP) ? d.softcap * kLog2e : 0.0f;
     kp.out_scale = p->fp8 ? d.v_scale : 1.0f;
 
-    if (pl.path == 3) {
+    if (pl.path == 3 && pl.stream_k) {
+        const int rows_per_slot = pl.block_q * p->group;
+        const size_t slots = (size_t)a->num_seqs * d.num_kv_heads + kMaxStreamKWorkers;
+        const size_t need = stream_k_bytes(*p, a->num_seqs, rows_per_slot);
+        if (!a->workspace || a->workspace_bytes < need)
+            return fail(UA_ERR_WORKSPACE, "split path needs %zu workspace bytes, got %zu", need,
+                        a->workspace ? a->workspace_bytes : (size_t)0);
+        if ((uintptr_t)a->workspace & 255)
+            return fail(UA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        float* ws = static_cast<float*>(a->workspace);
+        const size_t rows = slots * rows_per_slot;
+        kp.ws_o = ws;
+        kp.ws_m = ws + rows * d.head_dim;
+        kp.ws_l = kp.ws_m + rows;
+    } else if (pl.path == 3) {
         const size_t rows = (size_t)a->total_q * d.num_q_heads;
         const size_t need = rows * (size_t)pl.num_segments * row_bytes(*p);
         if (!a->workspace || a->workspace_bytes < need)
@@ -312,6 +354,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     l.q_dtype = d.q_dtype;
     l.kv_fp8 = p->fp8;
     for (int i = 0; i < 3; ++i) l.grid[i] = pl.grid[i];
+    l.stream_k = pl.stream_k;
     l.reduce_rows = a->total_q * d.num_q_heads;
     for (int i = 0; i < 3; ++i) l.events[i] = static_cast<hipEvent_t>(a->timing_events[i]);
 

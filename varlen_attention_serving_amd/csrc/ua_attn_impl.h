@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ua.h"
 #include "ua_internal.h"
 
@@ -149,26 +151,265 @@ __device__ __forceinline__ KeyRange key_range(uint32_t flags, int window, int s_
     return r;
 }
 
+
+// ---------------------------------------------------------------------------
+// K/V tile gather: global -> registers -> padded LDS
+// ---------------------------------------------------------------------------
+
+template <int D, int NW, int BN, bool FP8>
+struct TileGeom {
+    static constexpr int NT = NW * 64;
+    static constexpr int KSTR = D + kKPad;
+    static constexpr int VSTR = D + kVPad;
+    static constexpr int ESZ = FP8 ? 1 : 2;   // bytes per cached element
+    static constexpr int EPC = 16 / ESZ;      // cached elements per 16-byte chunk
+    static constexpr int CPR = D / EPC;       // chunks per key row
+    static_assert(NT % CPR == 0, "a thread's chunks must share one column");
+    static constexpr int RSTEP = NT / CPR;    // key rows covered per pass of the workgroup
+    static_assert(BN % RSTEP == 0, "tile rows must divide evenly");
+    static constexpr int NCH = BN / RSTEP;    // chunks per thread per tile (K, and again V)
+    static constexpr int NKT = BN / 32;       // 32-key sub-tiles (S^T accumulators)
+    static constexpr int NDT = D / 32;        // 32-wide d tiles (O^T accumulators)
+    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shapes");
+};
+
+// Each thread owns one 16-byte column chunk of NCH key rows of a tile.  Block
+// ids are fetched one tile ahead of the K/V loads that use them, so a tile's
+// gather never waits on a block-table read.  Loads are branch-free: a key past
+// S_k reads the sequence's last valid slot and is replaced by zeros.
+template <int D, int NW, int BN, typename QT, bool FP8>
+struct KvLoader {
+    typedef TileGeom<D, NW, BN, FP8> G;
+    u32x4 kreg[G::NCH], vreg[G::NCH];
+    int phys[G::NCH];
+    int cc, row0;
+
+    __device__ __forceinline__ void init(int tid) {
+        cc = tid % G::CPR;
+        row0 = tid / G::CPR;
+    }
+    __device__ __forceinline__ void ids(const int32_t* bt_row, int t, int s_k, int lb) {
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int key = min(t * BN + row0 + i * G::RSTEP, s_k - 1);
+            phys[i] = bt_row[key >> lb];
+        }
+    }
+    // base_k / base_v point at element (slot 0, head, 0) of the caches (bytes)
+    __device__ __forceinline__ void load(const unsigned char* base_k, const unsigned char* base_v,
+                                         int t, int s_k, int lb, int64_t slot_bytes) {
+        const int bmask = (1 << lb) - 1;
+        const int col = cc * G::EPC * G::ESZ;
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int key = t * BN + row0 + i * G::RSTEP;
+            const int kc = min(key, s_k - 1);
+            const int64_t off = (((int64_t)phys[i] << lb) + (kc & bmask)) * slot_bytes + col;
+            u32x4 kw = *reinterpret_cast<const u32x4*>(base_k + off);
+            u32x4 vw = *reinterpret_cast<const u32x4*>(base_v + off);
+            const bool ok = key < s_k;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            kreg[i] = ok ? kw : z;
+            vreg[i] = ok ? vw : z;
+        }
+    }
+    __device__ __forceinline__ void store(unsigned short* k_lds, unsigned short* v_lds) const {
+        typedef QType<QT> Q;
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int row = row0 + i * G::RSTEP;
+            if (FP8) {
+                // 16 codes -> 16 elements of the Q type (two 16-byte LDS writes)
+                u32x4 k0, k1, v0, v1;
+                u32x2 t;
+                t = Q::cvt_fp8x4(kreg[i][0]); k0[0] = t[0]; k0[1] = t[1];
+                t = Q::cvt_fp8x4(kreg[i][1]); k0[2] = t[0]; k0[3] = t[1];
+                t = Q::cvt_fp8x4(kreg[i][2]); k1[0] = t[0]; k1[1] = t[1];
+                t = Q::cvt_fp8x4(kreg[i][3]); k1[2] = t[0]; k1[3] = t[1];
+                t = Q::cvt_fp8x4(vreg[i][0]); v0[0] = t[0]; v0[1] = t[1];
+                t = Q::cvt_fp8x4(vreg[i][1]); v0[2] = t[0]; v0[3] = t[1];
+                t = Q::cvt_fp8x4(vreg[i][2]); v1[0] = t[0]; v1[1] = t[1];
+                t = Q::cvt_fp8x4(vreg[i][3]); v1[2] = t[0]; v1[3] = t[1];
+                *reinterpret_cast<u32x4*>(&k_lds[row * G::KSTR + cc * 16]) = k0;
+                *reinterpret_cast<u32x4*>(&k_lds[row * G::KSTR + cc * 16 + 8]) = k1;
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + cc * 16]) = v0;
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + cc * 16 + 8]) = v1;
+            } else {
+                *reinterpret_cast<u32x4*>(&k_lds[row * G::KSTR + cc * 8]) = kreg[i];
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + cc * 8]) = vreg[i];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// One wave's 32 query rows against one KV tile in LDS
+// ---------------------------------------------------------------------------
+
+// Per-lane facts of the lane's query row.
+struct RowCtx {
+    int ctx;     // S_k - q_len of the row's sequence
+    int kmin;    // first visible key
+    int kmax;    // last visible key
+    float slope2;  // ALiBi slope in log2 units (0 when off)
+};
+
+// Rows of one q-block: pos_local = r / g, head_local = r % g.
+struct RowInfo {
+    bool ok;
+    int tok, head;
+    RowCtx rc;
+};
+
+__device__ __forceinline__ RowInfo row_info(const UaKernelParams& p, int r, int hk, int q_start,
+                                            int q_len, int s_k, int p0) {
+    RowInfo ri;
+    const int pr = r / p.group;
+    const int hr = r - pr * p.group;
+    ri.ok = r < p.rows_used && p0 + pr < q_len;
+    ri.tok = q_start + p0 + pr;
+    ri.head = hk * p.group + hr;
+    const int q_abs = s_k - q_len + p0 + pr;
+    ri.rc.ctx = s_k - q_len;
+    ri.rc.kmax = (p.flags & UA_FLAG_CAUSAL) ? min(q_abs, s_k - 1) : s_k - 1;
+    ri.rc.kmin = (p.flags & UA_FLAG_WINDOW) ? q_abs - p.window + 1 : 0;
+    ri.rc.slope2 = (p.flags & UA_FLAG_ALIBI) ? p.slopes[ri.head] * kLog2e : 0.0f;
+    return ri;
+}
+
+// Q fragments: B operand of S^T = K Q^T; lane holds Q[row][16 kc + 8 half + 0..7].
+template <int D, typename QT>
+__device__ __forceinline__ void load_q(const UaKernelParams& p, const RowInfo& ri, int half,
+                                       typename QType<QT>::v8 (&qf)[D / 16]) {
+    typedef typename QType<QT>::v8 v8;
+    const QT* qp = reinterpret_cast<const QT*>(p.q) + (int64_t)ri.tok * p.q_stride_tok +
+                   (int64_t)ri.head * D + 8 * half;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ri.ok) w = *reinterpret_cast<const u32x4*>(qp + 16 * kc);
+        qf[kc] = __builtin_bit_cast(v8, w);
+    }
+}
+
+// scale -> softcap -> ALiBi -> masks (log2 units), the online-softmax update,
+// then O^T += V^T P^T.  key0 is the tile's first key position.
+template <int D, int BN, typename QT>
+__device__ __forceinline__ void attend_tile(const UaKernelParams& p,
+                                            const unsigned short* __restrict__ k_lds,
+                                            const unsigned short* __restrict__ v_lds,
+                                            const typename QType<QT>::v8 (&qf)[D / 16],
+                                            f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                            int key0, bool need_mask, const RowCtx& rc,
+                                            int k_frag, int v_frag, int half) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    constexpr int KSTR = D + kKPad;
+    constexpr int VSTR = D + kVPad;
+    constexpr int NKT = BN / 32;
+    constexpr int NDT = D / 32;
+
+    f32x16 sacc[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+            v8 a = *reinterpret_cast<const v8*>(&k_lds[k_frag + kt * 32 * KSTR + 16 * kc]);
+            sacc[kt] = Q::mma(a, qf[kc], sacc[kt]);
+        }
+    }
+
+    const bool softcap = p.flags & UA_FLAG_SOFTCAP;
+    const bool alibi = p.flags & UA_FLAG_ALIBI;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+            const float x = sacc[kt][i];
+            float sv = softcap ? p.softcap_out * tanh_f32(x * p.softcap_in) : x * p.qk_scale_log2;
+            sv = alibi ? sv + rc.slope2 * (float)(key - rc.ctx) : sv;
+            sv = (need_mask && (key < rc.kmin || key > rc.kmax)) ? -INFINITY : sv;
+            sacc[kt][i] = sv;
+            mt = fmaxf(mt, sv);
+        }
+    }
+    mt = fmaxf(mt, xor32(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+
+#pragma unroll
+    for (int kc = 0; kc < BN / 16; ++kc) {
+        const int kt = kc >> 1, q8 = (kc & 1) * 8;
+        v8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            QT e = (QT)fast_exp2(sacc[kt][q8 + j] - m_use);
+            l_run += (float)e;
+            pf[j] = e;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int off = v_frag + kc * 16 * VSTR + dt * 32;
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off]);
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + 8 * VSTR]);
+            u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
+            oacc[dt] = Q::mma(__builtin_bit_cast(v8, w), pf, oacc[dt]);
+        }
+    }
+}
+
+// per-lane LDS offsets of the K fragment read and of the transposing V read
+template <int D>
+__device__ __forceinline__ int k_frag_offset(int lane) {
+    return (lane & 31) * (D + kKPad) + 8 * (lane >> 5);
+}
+template <int D>
+__device__ __forceinline__ int v_frag_offset(int lane) {
+    const int g16 = lane >> 4;
+    return (4 * (g16 >> 1) + ((lane & 15) >> 2)) * (D + kVPad) + 16 * (g16 & 1) + 4 * (lane & 3);
+}
+
+// Un-normalised partial of the lane's row: o (fp32), the running max m (log2
+// units) and the denominator l, at workspace row `rid`.
+template <int D>
+__device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t rid, int half,
+                                              const f32x16 (&oacc)[D / 32], float m, float l) {
+    float* wo = p.ws_o + rid * D + 4 * half;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+            f32x4 v = {oacc[dt][4 * ig], oacc[dt][4 * ig + 1], oacc[dt][4 * ig + 2],
+                       oacc[dt][4 * ig + 3]};
+            *reinterpret_cast<f32x4*>(wo + 32 * dt + 8 * ig) = v;
+        }
+    if (half == 0) {
+        p.ws_m[rid] = m;
+        p.ws_l[rid] = l;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2D query-tile kernel and the segmented 3D split-KV kernel
+// ---------------------------------------------------------------------------
+
 template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
-    constexpr int NT = NW * 64;
-    constexpr int KSTR = D + kKPad;
-    constexpr int VSTR = D + kVPad;
-    constexpr int ESZ = FP8 ? 1 : 2;       // bytes per cached element
-    constexpr int EPC = 16 / ESZ;          // cached elements per 16-byte chunk
-    constexpr int CPR = D / EPC;           // chunks per key row
-    static_assert(NT % CPR == 0, "a thread's chunks must share one column");
-    constexpr int RSTEP = NT / CPR;        // key rows covered per pass of the workgroup
-    static_assert(BN % RSTEP == 0, "tile rows must divide evenly");
-    constexpr int NCH = BN / RSTEP;        // chunks per thread per tile (K, and again V)
-    constexpr int NKT = BN / 32;           // 32-key sub-tiles (S^T accumulators)
-    constexpr int NDT = D / 32;            // 32-wide d tiles (O^T accumulators)
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shapes");
+    typedef TileGeom<D, NW, BN, FP8> G;
 
-    __shared__ __attribute__((aligned(16))) unsigned short k_lds[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * VSTR];
+    __shared__ __attribute__((aligned(16))) unsigned short k_lds[BN * G::KSTR];
+    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * G::VSTR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -203,200 +444,66 @@ __global__ __launch_bounds__(NW * 64) void ua_attn_kernel(UaKernelParams p) {
         t_hi = min(t_hi, a + p.tiles_per_seg);
     }
 
-    // ---- this lane's query row ----
-    const int r = wave * 32 + (lane & 31);
-    const int pr = r / p.group;
-    const int hr = r - pr * p.group;
-    const bool row_ok = r < p.rows_used && p0 + pr < q_len;
-    const int tok = q_start + p0 + pr;
-    const int head = hk * p.group + hr;
-    const int q_abs = ctx + p0 + pr;
-    const bool causal = p.flags & UA_FLAG_CAUSAL;
-    const int kmax_row = causal ? min(q_abs, s_k - 1) : s_k - 1;
-    const int kmin_row = (p.flags & UA_FLAG_WINDOW) ? q_abs - p.window + 1 : 0;
+    const RowInfo ri = row_info(p, wave * 32 + (lane & 31), hk, q_start, q_len, s_k, p0);
     const int r0 = wave * 32;
     const bool wave_active = r0 < p.rows_used && p0 + r0 / p.group < q_len;
-
-    // Q fragments: B operand of S^T = K Q^T, lane holds Q[row][16 kc + 8 half + 0..7]
     v8 qf[D / 16];
-    {
-        const QT* qp = reinterpret_cast<const QT*>(p.q) + (int64_t)tok * p.q_stride_tok +
-                       (int64_t)head * D + 8 * half;
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (row_ok) w = *reinterpret_cast<const u32x4*>(qp + 16 * kc);
-            qf[kc] = __builtin_bit_cast(v8, w);
-        }
-    }
-    const float slope2 = (p.flags & UA_FLAG_ALIBI) ? p.slopes[head] * kLog2e : 0.0f;
+    load_q<D, QT>(p, ri, half, qf);
 
     // ---- running softmax state (log2 units) ----
     float m_run = -INFINITY;
     float l_run = 0.0f;
     if (!SPLIT && (p.flags & UA_FLAG_SINKS)) {
         // the sink is one more softmax column: start from (m, l) = (sink, 1)
-        m_run = p.sinks[head] * kLog2e;
+        m_run = p.sinks[ri.head] * kLog2e;
         l_run = half == 0 ? 1.0f : 0.0f;
     }
-    f32x16 oacc[NDT];
+    f32x16 oacc[G::NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+    for (int dt = 0; dt < G::NDT; ++dt) oacc[dt] = f32x16{};
 
-    // ---- tile loader: chunk column and rows of this thread ----
-    const int cc = tid % CPR;
-    const int row0 = tid / CPR;
     const int lb = p.block_size_log2;
-    const int bmask = (1 << lb) - 1;
     const int32_t* bt = p.block_table + (int64_t)s * p.bt_stride;
-    const unsigned char* kbase =
-        reinterpret_cast<const unsigned char*>(p.k) + ((int64_t)hk * D + cc * EPC) * ESZ;
-    const unsigned char* vbase =
-        reinterpret_cast<const unsigned char*>(p.v) + ((int64_t)hk * D + cc * EPC) * ESZ;
-    const int64_t slot_bytes = p.kv_slot_stride * ESZ;
+    const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
+    const unsigned char* base_k =
+        reinterpret_cast<const unsigned char*>(p.k) + (int64_t)hk * D * G::ESZ;
+    const unsigned char* base_v =
+        reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * G::ESZ;
+    KvLoader<D, NW, BN, QT, FP8> ld;
+    ld.init(tid);
+    const int k_frag = k_frag_offset<D>(lane);
+    const int v_frag = v_frag_offset<D>(lane);
 
-    u32x4 kreg[NCH], vreg[NCH];
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int key = t * BN + row0 + i * RSTEP;
-            u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-            if (key < s_k) {
-                const int64_t phys = bt[key >> lb];
-                const int64_t off = ((phys << lb) + (key & bmask)) * slot_bytes;
-                kw = *reinterpret_cast<const u32x4*>(kbase + off);
-                vw = *reinterpret_cast<const u32x4*>(vbase + off);
-            }
-            kreg[i] = kw;
-            vreg[i] = vw;
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int row = row0 + i * RSTEP;
-            if (FP8) {
-                // 16 codes -> 16 elements of the Q type (two 16-byte LDS writes)
-                u32x4 k0, k1, v0, v1;
-                u32x2 t;
-                t = Q::cvt_fp8x4(kreg[i][0]); k0[0] = t[0]; k0[1] = t[1];
-                t = Q::cvt_fp8x4(kreg[i][1]); k0[2] = t[0]; k0[3] = t[1];
-                t = Q::cvt_fp8x4(kreg[i][2]); k1[0] = t[0]; k1[1] = t[1];
-                t = Q::cvt_fp8x4(kreg[i][3]); k1[2] = t[0]; k1[3] = t[1];
-                t = Q::cvt_fp8x4(vreg[i][0]); v0[0] = t[0]; v0[1] = t[1];
-                t = Q::cvt_fp8x4(vreg[i][1]); v0[2] = t[0]; v0[3] = t[1];
-                t = Q::cvt_fp8x4(vreg[i][2]); v1[0] = t[0]; v1[1] = t[1];
-                t = Q::cvt_fp8x4(vreg[i][3]); v1[2] = t[0]; v1[3] = t[1];
-                *reinterpret_cast<u32x4*>(&k_lds[row * KSTR + cc * 16]) = k0;
-                *reinterpret_cast<u32x4*>(&k_lds[row * KSTR + cc * 16 + 8]) = k1;
-                *reinterpret_cast<u32x4*>(&v_lds[row * VSTR + cc * 16]) = v0;
-                *reinterpret_cast<u32x4*>(&v_lds[row * VSTR + cc * 16 + 8]) = v1;
-            } else {
-                *reinterpret_cast<u32x4*>(&k_lds[row * KSTR + cc * 8]) = kreg[i];
-                *reinterpret_cast<u32x4*>(&v_lds[row * VSTR + cc * 8]) = vreg[i];
-            }
-        }
-    };
-
-    // per-lane LDS offsets of the K fragment read and the transposing V read
-    const int k_frag = (lane & 31) * KSTR + 8 * half;
-    const int g16 = lane >> 4;
-    const int v_frag = (4 * (g16 >> 1) + ((lane & 15) >> 2)) * VSTR + 16 * (g16 & 1) + 4 * (lane & 3);
-
-    load_tile(t_lo);
+    ld.ids(bt, t_lo, s_k, lb);
+    ld.load(base_k, base_v, t_lo, s_k, lb, slot_bytes);
+    if (t_lo + 1 < t_hi) ld.ids(bt, t_lo + 1, s_k, lb);
     for (int t = t_lo; t < t_hi; ++t) {
         __syncthreads();  // every wave is done with the previous tile
-        store_tile();
+        ld.store(k_lds, v_lds);
         __syncthreads();
-        if (t + 1 < t_hi) load_tile(t + 1);  // in flight while this tile computes
-        if (!wave_active) continue;
-
-        // S^T = K Q^T for BN keys
-        f32x16 sacc[NKT];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            sacc[kt] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < D / 16; ++kc) {
-                v8 a = *reinterpret_cast<const v8*>(&k_lds[k_frag + kt * 32 * KSTR + 16 * kc]);
-                sacc[kt] = Q::mma(a, qf[kc], sacc[kt]);
-            }
+        if (t + 1 < t_hi) {
+            ld.load(base_k, base_v, t + 1, s_k, lb, slot_bytes);  // in flight during compute
+            if (t + 2 < t_hi) ld.ids(bt, t + 2, s_k, lb);
         }
-
-        // scale -> softcap -> ALiBi -> masks (log2 units)
+        if (!wave_active) continue;
         const int key0 = t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-                float x = sacc[kt][i];
-                float sv = (p.flags & UA_FLAG_SOFTCAP) ? p.softcap_out * tanh_f32(x * p.softcap_in)
-                                                       : x * p.qk_scale_log2;
-                if (p.flags & UA_FLAG_ALIBI) sv += slope2 * (float)(key - ctx);
-                if (need_mask) sv = (key >= kmin_row && key <= kmax_row) ? sv : -INFINITY;
-                sacc[kt][i] = sv;
-                mt = fmaxf(mt, sv);
-            }
-        }
-        mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-
-        // O^T += V^T P^T, 16 keys per step in accumulator order
-#pragma unroll
-        for (int kc = 0; kc < BN / 16; ++kc) {
-            const int kt = kc >> 1, q8 = (kc & 1) * 8;
-            v8 pf;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                QT e = (QT)fast_exp2(sacc[kt][q8 + j] - m_use);
-                l_run += (float)e;
-                pf[j] = e;
-            }
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int off = v_frag + kc * 16 * VSTR + dt * 32;
-                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off]);
-                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + 8 * VSTR]);
-                u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                oacc[dt] = Q::mma(__builtin_bit_cast(v8, w), pf, oacc[dt]);
-            }
-        }
+        attend_tile<D, BN, QT>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+                               k_frag, v_frag, half);
     }
 
     if (!wave_active) return;
     const float l_tot = l_run + xor32(l_run);
-    if (!row_ok) return;
+    if (!ri.ok) return;
     if (SPLIT) {
-        const int64_t rid = ((int64_t)tok * p.num_q_heads + head) * p.num_segments + seg;
-        float* wo = p.ws_o + rid * D + 4 * half;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int ig = 0; ig < 4; ++ig) {
-                f32x4 v = {oacc[dt][4 * ig], oacc[dt][4 * ig + 1], oacc[dt][4 * ig + 2],
-                           oacc[dt][4 * ig + 3]};
-                *reinterpret_cast<f32x4*>(wo + 32 * dt + 8 * ig) = v;
-            }
-        if (half == 0) {
-            p.ws_m[rid] = m_run;
-            p.ws_l[rid] = l_tot;
-        }
+        const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
+        write_partial<D>(p, rid, half, oacc, m_run, l_tot);
     } else {
         const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
-        QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)tok * p.o_stride_tok + (int64_t)head * D +
-                 4 * half;
+        QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)ri.tok * p.o_stride_tok +
+                 (int64_t)ri.head * D + 4 * half;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < G::NDT; ++dt)
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
                 typename Q::v4 v;
@@ -407,10 +514,243 @@ __global__ __launch_bounds__(NW * 64) void ua_attn_kernel(UaKernelParams p) {
     }
 }
 
-// Log-sum-exp merge of the split partials (section 5: re-base each segment to
-// the global max and sum), sinks folded in once, then /L and the cast.  One
-// wave per (token, query head); four per workgroup.
-template <int D, typename QT>
+// ---------------------------------------------------------------------------
+// Stream-K split for decode-shaped batches
+// ---------------------------------------------------------------------------
+//
+// When every sequence's query rows fit one q-block (decode and short chunks),
+// the units of KV work are the (sequence, kv-head) pairs, taken in the order
+// p = s * H_k + h.  Flatten their KV tiles into one index space of T tiles and
+// give worker j of W the contiguous range [floor(jT/W), floor((j+1)T/W)).  All
+// workers then carry equal work whatever the length mix, and each pays the
+// metadata prelude once.  A worker writes one partial per pair it touches, at
+// slot p + j: along a worker's range p and j never decrease together, so p + j
+// is unique per (pair, worker).  The reduce finds a pair's workers from its
+// first and last flattened tile.
+
+// Per-sequence facts of that geometry, one sequence per lane.
+struct SeqLane {
+    int q_start, q_len, s_k, t_lo, n;  // n = KV tiles of the sequence's q-block
+};
+
+template <int BN>
+__device__ __forceinline__ SeqLane seq_lane(const UaKernelParams& p, int s) {
+    SeqLane r = {0, 0, 0, 0, 0};
+    if (s >= p.num_seqs) return r;
+    r.q_start = p.cu_q[s];
+    r.q_len = p.cu_q[s + 1] - r.q_start;
+    r.s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
+    if (r.q_len <= 0) return r;
+    const KeyRange kr = key_range(p.flags, p.window, r.s_k, r.s_k - r.q_len, 0, r.q_len - 1);
+    r.t_lo = kr.lo / BN;
+    r.n = max(0, (kr.hi + BN - 1) / BN - r.t_lo);
+    return r;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// Total tiles T and, for flattened tile x, the sequence holding it and that
+// sequence's first flattened tile.  Every lane of the wave gets the results.
+template <int BN>
+__device__ __forceinline__ int sk_total(const UaKernelParams& p) {
+    int total = 0;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
+        total += readlane(wave_incl_scan(q.n * p.num_kv_heads), 63);
+    }
+    return total;
+}
+
+template <int BN>
+__device__ __forceinline__ int sk_locate(const UaKernelParams& p, int64_t x, int* seq_first) {
+    int carry = 0;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
+        const int v = q.n * p.num_kv_heads;
+        const int incl = wave_incl_scan(v);
+        const uint64_t hit = __ballot((int64_t)carry + incl > x);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            *seq_first = carry + readlane(incl - v, l);
+            return base + l;
+        }
+        carry += readlane(incl, 63);
+    }
+    *seq_first = carry;
+    return p.num_seqs;
+}
+
+// worker j of W owns flattened tiles [floor(jT/W), floor((j+1)T/W)); the
+// worker holding tile x is ceil((x+1) W / T) - 1
+__device__ __forceinline__ int sk_worker_of(int64_t x, int64_t T, int64_t W) {
+    return (int)(((x + 1) * W + T - 1) / T - 1);
+}
+
+// A position in the flattened tile space with the facts of its pair.
+struct SkPos {
+    int s, h, t, t_lo, t_end, q_start, q_len, s_k;
+};
+
+template <int BN>
+__device__ __forceinline__ SkPos sk_pos(const UaKernelParams& p, int s, int h, int t) {
+    const SeqLane q = seq_lane<BN>(p, s);  // uniform s: every lane reads the same facts
+    SkPos r;
+    r.s = s; r.h = h; r.t = t;
+    r.t_lo = q.t_lo; r.t_end = q.t_lo + q.n;
+    r.q_start = q.q_start; r.q_len = q.q_len; r.s_k = q.s_k;
+    return r;
+}
+
+// the next tile of the flattened order (callers never step past their range)
+template <int BN>
+__device__ __forceinline__ SkPos sk_next(const UaKernelParams& p, const SkPos& c) {
+    SkPos r = c;
+    if (c.t + 1 < c.t_end) {
+        r.t = c.t + 1;
+        return r;
+    }
+    if (c.h + 1 < p.num_kv_heads) {
+        r.h = c.h + 1;
+        r.t = c.t_lo;
+        return r;
+    }
+    int s = c.s + 1;
+    SeqLane q = seq_lane<BN>(p, s);
+    while (q.n == 0 && s + 1 < p.num_seqs) q = seq_lane<BN>(p, ++s);
+    r.s = s; r.h = 0; r.t = q.t_lo; r.t_lo = q.t_lo; r.t_end = q.t_lo + q.n;
+    r.q_start = q.q_start; r.q_len = q.q_len; r.s_k = q.s_k;
+    return r;
+}
+
+// first flattened tile of sequence s, its tile count and the total T
+template <int BN>
+__device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int* n_s, int* total) {
+    int carry = 0, first = 0, n = 0;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
+        const int v = q.n * p.num_kv_heads;
+        const int incl = wave_incl_scan(v);
+        if (s >= base && s < base + 64) {
+            first = carry + readlane(incl - v, s - base);
+            n = readlane(q.n, s - base);
+        }
+        carry += readlane(incl, 63);
+    }
+    *n_s = n;
+    *total = carry;
+    return first;
+}
+
+template <int D, int BN, typename QT, bool FP8>
+__global__ __launch_bounds__(64) void ua_decode_sk_kernel(UaKernelParams p) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    typedef TileGeom<D, 1, BN, FP8> G;
+    static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
+
+    __shared__ __attribute__((aligned(16))) unsigned short k_lds[BN * G::KSTR];
+    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * G::VSTR];
+
+    const int lane = threadIdx.x;
+    const int half = lane >> 5;
+    const int64_t W = gridDim.x;
+    const int64_t j = blockIdx.x;
+    const int T = sk_total<BN>(p);
+    const int64_t A = j * T / W;
+    const int64_t B = (j + 1) * T / W;
+    if (A >= B) return;
+
+    int seq_first;
+    const int s0 = sk_locate<BN>(p, A, &seq_first);
+    SkPos pc = sk_pos<BN>(p, s0, 0, 0);
+    {
+        const int n = pc.t_end - pc.t_lo;
+        const int off = (int)(A - seq_first);
+        pc.h = off / n;
+        pc.t = pc.t_lo + (off - pc.h * n);
+    }
+    SkPos p1 = pc, p2 = pc;
+    if (A + 1 < B) p1 = sk_next<BN>(p, pc);
+    if (A + 2 < B) p2 = sk_next<BN>(p, p1);
+
+    const int lb = p.block_size_log2;
+    const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
+    const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
+    const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
+    auto bt_row = [&](const SkPos& q) { return p.block_table + (int64_t)q.s * p.bt_stride; };
+    auto hoff = [&](const SkPos& q) { return (int64_t)q.h * D * G::ESZ; };
+
+    KvLoader<D, 1, BN, QT, FP8> ld;
+    ld.init(lane);
+    const int k_frag = k_frag_offset<D>(lane);
+    const int v_frag = v_frag_offset<D>(lane);
+    ld.ids(bt_row(pc), pc.t, pc.s_k, lb);
+    ld.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
+    if (A + 1 < B) ld.ids(bt_row(p1), p1.t, p1.s_k, lb);
+
+    // state of the pair being accumulated
+    RowInfo ri;
+    KeyRange kr;
+    v8 qf[D / 16];
+    f32x16 oacc[G::NDT];
+    float m_run, l_run;
+    auto begin_pair = [&](const SkPos& q) {
+        ri = row_info(p, lane & 31, q.h, q.q_start, q.q_len, q.s_k, 0);
+        kr = key_range(p.flags, p.window, q.s_k, q.s_k - q.q_len, 0, q.q_len - 1);
+        load_q<D, QT>(p, ri, half, qf);
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) oacc[dt] = f32x16{};
+    };
+    begin_pair(pc);
+
+    for (int64_t x = A; x < B; ++x) {
+        __syncthreads();
+        ld.store(k_lds, v_lds);
+        __syncthreads();
+        if (x + 1 < B) {
+            ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
+            if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb);
+        }
+        const int key0 = pc.t * BN;
+        const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
+        attend_tile<D, BN, QT>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+                               k_frag, v_frag, half);
+        if (x + 1 == B || pc.t + 1 == pc.t_end) {
+            const float l_tot = l_run + xor32(l_run);
+            if (ri.ok) {
+                const int64_t slot = (int64_t)pc.s * p.num_kv_heads + pc.h + j;
+                write_partial<D>(p, slot * p.rows_used + (lane & 31), half, oacc, m_run, l_tot);
+            }
+            if (x + 1 < B) begin_pair(p1);
+        }
+        pc = p1;
+        p1 = p2;
+        if (x + 3 < B) p2 = sk_next<BN>(p, p2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of split partials
+// ---------------------------------------------------------------------------
+//
+// The re-base of section 5 of the unified page: M = max over partials (and the
+// sink), L = sum l_i 2^(m_i - M) (+ 2^(sink - M)), O = sum o_i 2^(m_i - M) / L,
+// then the cast.  Partials with m = -inf saw no visible key and are skipped.
+// One wave per (token, query head); four per workgroup.  SK selects the
+// stream-K slot layout, else the segmented one.
+template <int D, typename QT, bool SK>
 __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_t n_rows) {
     constexpr int EPL = D / 64;  // elements per lane
     const int lane = threadIdx.x & 63;
@@ -421,32 +761,63 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
     const int s = token_seq(p.cu_q, p.num_seqs, tok);
     const int q_start = p.cu_q[s];
     const int q_len = p.cu_q[s + 1] - q_start;
-    const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
-    const int ctx = s_k - q_len;
-    const int p0 = ((tok - q_start) / p.block_q) * p.block_q;
-    const int p_last = min(p0 + p.block_q, q_len) - 1;
-    const KeyRange kr = key_range(p.flags, p.window, s_k, ctx, p0, p_last);
-    const int t_lo = kr.lo / p.tile_n;
-    const int t_hi = (kr.hi + p.tile_n - 1) / p.tile_n;
-    const int n_live = t_hi > t_lo ? min(p.num_segments,
-                                         (t_hi - t_lo + p.tiles_per_seg - 1) / p.tiles_per_seg)
-                                   : 0;
 
-    const int64_t base = row * p.num_segments;
+    // partials of this row: workspace rows first + g * stride for g < count;
+    // stream-K skips workers whose flattened range is empty
+    int64_t first, stride;
+    int count;
+    int64_t T = 0, W = 1;
+    int j0 = 0;
+    if (SK) {
+        int n, total;
+        const int xs = sk_seq_prefix<kSkTile>(p, s, &n, &total);
+        const int hk = head / p.group;
+        const int64_t x0 = xs + (int64_t)hk * n;
+        T = total;
+        W = p.sk_workers;
+        j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
+        const int j1 = T > 0 ? sk_worker_of(x0 + n - 1, T, W) : 0;
+        const int r = (tok - q_start) * p.group + (head - hk * p.group);
+        first = ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r;
+        stride = p.rows_used;
+        count = (n > 0 && T > 0) ? j1 - j0 + 1 : 0;
+    } else {
+        const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
+        const int ctx = s_k - q_len;
+        const int p0 = ((tok - q_start) / p.block_q) * p.block_q;
+        const int p_last = min(p0 + p.block_q, q_len) - 1;
+        const KeyRange kr = key_range(p.flags, p.window, s_k, ctx, p0, p_last);
+        const int t_lo = kr.lo / p.tile_n;
+        const int t_hi = (kr.hi + p.tile_n - 1) / p.tile_n;
+        first = row * p.num_segments;
+        stride = 1;
+        count = t_hi > t_lo ? min(p.num_segments, (t_hi - t_lo + p.tiles_per_seg - 1) /
+                                                      p.tiles_per_seg)
+                            : 0;
+    }
+    auto live = [&](int g) {
+        if (!SK) return true;
+        const int64_t j = j0 + g;
+        return j * T / W < (j + 1) * T / W;
+    };
+
     const bool sinks = p.flags & UA_FLAG_SINKS;
     const float sink2 = sinks ? p.sinks[head] * kLog2e : -INFINITY;
     float mx = sink2;
-    for (int g = 0; g < n_live; ++g) mx = fmaxf(mx, p.ws_m[base + g]);
+    for (int g = 0; g < count; ++g)
+        if (live(g)) mx = fmaxf(mx, p.ws_m[first + g * stride]);
     float L = sinks ? fast_exp2(sink2 - mx) : 0.0f;
     float acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-    for (int g = 0; g < n_live; ++g) {
-        const float mg = p.ws_m[base + g];
+    for (int g = 0; g < count; ++g) {
+        if (!live(g)) continue;
+        const int64_t rid = first + g * stride;
+        const float mg = p.ws_m[rid];
         if (mg == -INFINITY) continue;
         const float w = fast_exp2(mg - mx);
-        L += p.ws_l[base + g] * w;
-        const float* src = p.ws_o + (base + g) * D + lane * EPL;
+        L += p.ws_l[rid] * w;
+        const float* src = p.ws_o + rid * D + lane * EPL;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
     }
@@ -457,17 +828,57 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
     for (int e = 0; e < EPL; ++e) dst[e] = (QT)(acc[e] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+// workers of the stream-K split: as many single-wave workgroups as the device
+// holds at once (queried once per device and instantiation)
+template <typename K>
+int resident_workgroups(K kernel) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cache[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        cache[dev] = per_cu * cus;
+    }
+    return cache[dev];
+}
+
 template <int D, int NW, int BN, typename QT, bool FP8>
-hipError_t launch_attn(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
+hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t st) {
+    UaKernelParams p = p0;
     dim3 grid(l.grid[0], l.grid[1], l.grid[2]);
     hipError_t e = hipSuccess;
     if (l.events[0] && (e = hipEventRecord(l.events[0], st)) != hipSuccess) return e;
-    if (l.path == 3) {
+    const unsigned nb = (unsigned)((l.reduce_rows + 3) / 4);
+    if (l.path == 3 && l.stream_k) {
+        if constexpr (NW == 1) {
+            const int workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8>),
+                                         (int)kMaxStreamKWorkers);
+            p.sk_workers = workers;
+            hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8>), dim3(workers), dim3(64), 0,
+                               st, p);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
+            hipLaunchKernelGGL((ua_reduce_kernel<D, QT, true>), dim3(nb), dim3(256), 0, st, p,
+                               l.reduce_rows);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (l.path == 3) {
         hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true>), grid, dim3(NW * 64), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
-        const unsigned nb = (unsigned)((l.reduce_rows + 3) / 4);
-        hipLaunchKernelGGL((ua_reduce_kernel<D, QT>), dim3(nb), dim3(256), 0, st, p, l.reduce_rows);
+        hipLaunchKernelGGL((ua_reduce_kernel<D, QT, false>), dim3(nb), dim3(256), 0, st, p,
+                           l.reduce_rows);
     } else {
         hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false>), grid, dim3(NW * 64), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -38,7 +38,13 @@ struct UaKernelParams {
     float softcap_in;         // tau * k_scale / c
     float softcap_out;        // c * log2(e)
     float out_scale;          // v_scale for fp8 V, else 1
+    int32_t sk_workers;       // stream-K split: number of workers W
 };
+
+// Upper bound on stream-K workers (sizes the workspace before the device is known).
+constexpr int kMaxStreamKWorkers = 8192;
+// KV tile of the single-wave (decode) geometry, the only one the stream-K split uses.
+constexpr int kSkTile = 32;
 
 struct UaLaunch {
     int path;        // 2 or 3
@@ -48,6 +54,7 @@ struct UaLaunch {
     int q_dtype;     // UA_DTYPE_BF16 / UA_DTYPE_F16
     int kv_fp8;      // 1 when K/V are e4m3fn
     unsigned grid[3];
+    int stream_k;    // split path: 1 = stream-K workers (single-wave geometry)
     int64_t reduce_rows;  // split path: total_q * H_q
     hipEvent_t events[3]; // optional: before attention, between kernels, at the end
 };

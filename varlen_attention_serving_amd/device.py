@@ -12,7 +12,7 @@ _TORCH_VIEW = {B.UA_DTYPE_BF16: torch.bfloat16, B.UA_DTYPE_F16: torch.float16}
 
 
 def problem_desc(w, extra_flags: int = 0, max_total_q=None, max_seqlen_k=None,
-                 max_num_seqs=None) -> B.ua_problem_desc_t:
+                 max_num_seqs=None, split_segment_tiles: int = 0) -> B.ua_problem_desc_t:
     """Descriptor of workload ``w`` (a ``workloads.Workload``)."""
     flags = extra_flags
     if w.causal:
@@ -33,7 +33,8 @@ def problem_desc(w, extra_flags: int = 0, max_total_q=None, max_seqlen_k=None,
         max_num_seqs=max(1, w.num_seqs if max_num_seqs is None else max_num_seqs),
         max_blocks_per_seq=int(w.block_table.shape[1]),
         max_total_q=max(1, w.total_q if max_total_q is None else max_total_q),
-        max_seqlen_k=max(1, w.max_seqlen_k if max_seqlen_k is None else max_seqlen_k))
+        max_seqlen_k=max(1, w.max_seqlen_k if max_seqlen_k is None else max_seqlen_k),
+        split_segment_tiles=split_segment_tiles)
 
 
 class DeviceBatch:
