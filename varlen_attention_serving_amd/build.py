@@ -33,9 +33,9 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, extra=(), build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -46,21 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = True) -> str:
-    """Compile all sources for gfx950 and link ``libua.so`` (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int = 0, verbose: bool = True, defines=(), out: str = LIB,
+          build_dir: str = BUILD_DIR) -> str:
+    """Compile all sources for gfx950 and link ``libua.so`` (always rebuilds).
+    ``defines``/``out``/``build_dir`` serve experiment builds of variants."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, len(os.sched_getaffinity(0))))
+    extra = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, extra, build_dir), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -73,10 +73,22 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
     const ua_problem_desc_t& d = P.d;
     Plan pl{};
     // geometry: one wave of 32 rows when the rows of any q-block fit in it
-    // (decode-like batches), else four waves (128 rows) sharing each KV tile
+    // (decode-like batches), else four waves (128 rows) sharing each KV tile;
+    // 32-key tiles keep every variant at three or more waves per SIMD
     const bool small = (int64_t)std::max(max_q, 1) * P.group <= 32;
+#if defined(UA_EXPERIMENT_WIDE)
+    pl.waves = small ? 1 : UA_WIDE_WAVES;
+    pl.tile_n = small ? 32 : (d.head_dim >= 256 ? 32 : UA_WIDE_TILE_N);
+#else
     pl.waves = small ? 1 : 4;
-    pl.tile_n = small ? 32 : (d.head_dim >= 256 ? 32 : 64);
+    pl.tile_n = 32;
+#endif
+    {
+        // a tile must hold whole passes of the workgroup's 16-byte row chunks
+        const int chunks_per_row = d.head_dim * (P.fp8 ? 1 : 2) / 16;
+        const int rows_per_pass = pl.waves * 64 / chunks_per_row;
+        pl.tile_n = std::max(pl.tile_n, rows_per_pass);
+    }
     pl.block_m = 32 * pl.waves;
     pl.block_q = pl.block_m / P.group;
     pl.slots = total_q / pl.block_q + num_seqs;

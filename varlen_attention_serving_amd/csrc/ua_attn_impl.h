@@ -67,6 +67,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKPad = 8;   // K LDS row padding (elements)
 constexpr int kVPad = 32;  // V LDS row padding (elements)
+// Register budget: at least two resident waves per SIMD, so one wave's MFMAs
+// overlap another's softmax arithmetic and memory waits.
+#ifndef UA_MIN_WAVES_PER_SIMD
+#define UA_MIN_WAVES_PER_SIMD 2
+#endif
+constexpr int kMinWavesPerSimd = UA_MIN_WAVES_PER_SIMD;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -293,8 +299,9 @@ __device__ __forceinline__ void load_q(const UaKernelParams& p, const RowInfo& r
 }
 
 // scale -> softcap -> ALiBi -> masks (log2 units), the online-softmax update,
-// then O^T += V^T P^T.  key0 is the tile's first key position.
-template <int D, int BN, typename QT>
+// then O^T += V^T P^T.  key0 is the tile's first key position.  XFORM = false
+// compiles the plain scale for problems without softcap and ALiBi.
+template <int D, int BN, typename QT, bool XFORM>
 __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
                                             const unsigned short* __restrict__ k_lds,
                                             const unsigned short* __restrict__ v_lds,
@@ -320,30 +327,40 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         }
     }
 
-    const bool softcap = p.flags & UA_FLAG_SOFTCAP;
-    const bool alibi = p.flags & UA_FLAG_ALIBI;
+    // Scores to log2 units.  Without softcap/ALiBi the multiplier c > 0 keeps
+    // the order, so the max is taken on raw scores and the scale is folded
+    // into the exponent as one FMA: 2^(x c - m).
+    const bool softcap = XFORM && (p.flags & UA_FLAG_SOFTCAP);
+    const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
+    const float c = XFORM ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float x = sacc[kt][i];
-            float sv = softcap ? p.softcap_out * tanh_f32(x * p.softcap_in) : x * p.qk_scale_log2;
-            sv = alibi ? sv + rc.slope2 * (float)(key - rc.ctx) : sv;
+            float sv = sacc[kt][i];
+            if (XFORM) {
+                sv = softcap ? p.softcap_out * tanh_f32(sv * p.softcap_in) : sv * p.qk_scale_log2;
+                sv = alibi ? sv + rc.slope2 * (float)(key - rc.ctx) : sv;
+            }
             sv = (need_mask && (key < rc.kmin || key > rc.kmax)) ? -INFINITY : sv;
             sacc[kt][i] = sv;
             mt = fmaxf(mt, sv);
         }
     }
-    mt = fmaxf(mt, xor32(mt));
+    mt = fmaxf(mt, xor32(mt)) * c;
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    // O and l are re-based only when some row's max moved: elsewhere alpha is
+    // exactly 1, so skipping the multiply changes nothing.
+    if (__ballot(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_use);
+        l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+    }
+    m_run = m_new;
 
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
@@ -351,9 +368,9 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         v8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            QT e = (QT)fast_exp2(sacc[kt][q8 + j] - m_use);
-            l_run += (float)e;
-            pf[j] = e;
+            const float e = fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
+            l_run += e;
+            pf[j] = (QT)e;
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -402,8 +419,8 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // 2D query-tile kernel and the segmented 3D split-KV kernel
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void ua_attn_kernel(UaKernelParams p) {
+template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, bool XFORM>
+__global__ __launch_bounds__(NW * 64, kMinWavesPerSimd) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, NW, BN, FP8> G;
@@ -488,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) void ua_attn_kernel(UaKernelParams p) {
         if (!wave_active) continue;
         const int key0 = t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        attend_tile<D, BN, QT>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+        attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
                                k_frag, v_frag, half);
     }
 
@@ -651,8 +668,8 @@ __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int
     return first;
 }
 
-template <int D, int BN, typename QT, bool FP8>
-__global__ __launch_bounds__(64) void ua_decode_sk_kernel(UaKernelParams p) {
+template <int D, int BN, typename QT, bool FP8, bool XFORM>
+__global__ __launch_bounds__(64, kMinWavesPerSimd) void ua_decode_sk_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, 1, BN, FP8> G;
@@ -725,7 +742,7 @@ __global__ __launch_bounds__(64) void ua_decode_sk_kernel(UaKernelParams p) {
         }
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        attend_tile<D, BN, QT>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+        attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
                                k_frag, v_frag, half);
         if (x + 1 == B || pc.t + 1 == pc.t_end) {
             const float l_tot = l_run + xor32(l_run);
@@ -852,7 +869,7 @@ int resident_workgroups(K kernel) {
     return cache[dev];
 }
 
-template <int D, int NW, int BN, typename QT, bool FP8>
+template <int D, int NW, int BN, typename QT, bool FP8, bool XFORM>
 hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t st) {
     UaKernelParams p = p0;
     dim3 grid(l.grid[0], l.grid[1], l.grid[2]);
@@ -861,10 +878,10 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
     const unsigned nb = (unsigned)((l.reduce_rows + 3) / 4);
     if (l.path == 3 && l.stream_k) {
         if constexpr (NW == 1) {
-            const int workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8>),
+            const int workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>),
                                          (int)kMaxStreamKWorkers);
             p.sk_workers = workers;
-            hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8>), dim3(workers), dim3(64), 0,
+            hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>), dim3(workers), dim3(64), 0,
                                st, p);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
@@ -874,13 +891,13 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
             return hipErrorInvalidValue;
         }
     } else if (l.path == 3) {
-        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true>), grid, dim3(NW * 64), 0, st, p);
+        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XFORM>), grid, dim3(NW * 64), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
         hipLaunchKernelGGL((ua_reduce_kernel<D, QT, false>), dim3(nb), dim3(256), 0, st, p,
                            l.reduce_rows);
     } else {
-        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false>), grid, dim3(NW * 64), 0, st, p);
+        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false, XFORM>), grid, dim3(NW * 64), 0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
     }
@@ -889,21 +906,46 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
     return hipSuccess;
 }
 
-template <int D, typename QT, bool FP8>
-hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
-    constexpr int BN4 = D >= 256 ? 32 : 64;
-    if (l.waves == 1 && l.tile_n == 32) return launch_attn<D, 1, 32, QT, FP8>(p, l, st);
-    if (l.waves == 4 && l.tile_n == BN4) return launch_attn<D, 4, BN4, QT, FP8>(p, l, st);
+// a geometry is built only where every thread's tile rows divide evenly
+template <int D, int NW, int BN, bool FP8>
+constexpr bool geometry_ok() {
+    constexpr int cpr = D / (FP8 ? 16 : 8);
+    return (NW * 64) % cpr == 0 && BN % ((NW * 64) / cpr) == 0;
+}
+
+template <int D, int NW, int BN, typename QT, bool FP8, bool XFORM>
+hipError_t launch_if_built(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
+    if constexpr (geometry_ok<D, NW, BN, FP8>()) return launch_attn<D, NW, BN, QT, FP8, XFORM>(p, l, st);
     return hipErrorInvalidValue;
+}
+
+template <int D, typename QT, bool FP8, bool XFORM>
+hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
+    if (l.waves == 1 && l.tile_n == 32) return launch_if_built<D, 1, 32, QT, FP8, XFORM>(p, l, st);
+    if (l.waves == 4 && l.tile_n == 32) return launch_if_built<D, 4, 32, QT, FP8, XFORM>(p, l, st);
+    if constexpr (D <= 128) {
+        if (l.waves == 4 && l.tile_n == 64) return launch_if_built<D, 4, 64, QT, FP8, XFORM>(p, l, st);
+#if defined(UA_EXPERIMENT_WIDE)
+        if (l.waves == 8 && l.tile_n == 32) return launch_if_built<D, 8, 32, QT, FP8, XFORM>(p, l, st);
+        if (l.waves == 8 && l.tile_n == 64) return launch_if_built<D, 8, 64, QT, FP8, XFORM>(p, l, st);
+#endif
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, typename QT, bool FP8>
+hipError_t launch_xform(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
+    if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI)) return launch_geometry<D, QT, FP8, true>(p, l, st);
+    return launch_geometry<D, QT, FP8, false>(p, l, st);
 }
 
 template <int D>
 hipError_t launch_head_dim(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
     if (l.q_dtype == UA_DTYPE_BF16)
-        return l.kv_fp8 ? launch_geometry<D, __bf16, true>(p, l, st)
-                        : launch_geometry<D, __bf16, false>(p, l, st);
-    return l.kv_fp8 ? launch_geometry<D, _Float16, true>(p, l, st)
-                    : launch_geometry<D, _Float16, false>(p, l, st);
+        return l.kv_fp8 ? launch_xform<D, __bf16, true>(p, l, st)
+                        : launch_xform<D, __bf16, false>(p, l, st);
+    return l.kv_fp8 ? launch_xform<D, _Float16, true>(p, l, st)
+                    : launch_xform<D, _Float16, false>(p, l, st);
 }
 
 }  // namespace ua
