@@ -86,6 +86,48 @@ def load_traffic(workload, path_id):
     return t.get("bytes_per_launch")
 
 
+def _counter_per_launch(csv_path, kernel_substr, counter):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} in {csv_path}")
+    return float(np.mean(vals)), len(vals)
+
+
+def summarize_traffic(args):
+    """HBM bytes per launch of the attention kernel from rocprofv3 --pmc CSVs
+    (FETCH_SIZE and WRITE_SIZE runs of this bench, and of --copy-calibration),
+    each scaled by what the counter reads for the plain copy of known size."""
+    fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes = args.summarize_traffic
+    copy_bytes = int(copy_bytes)
+    cf, _ = _counter_per_launch(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_per_launch(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    out = {"workload": args.workload, "kernel_source_hash": kernel_source_hash(),
+           "copy_calibration_bytes": copy_bytes,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for name, sub in (("attention", "ua_decode_sk_kernel" if args.force != "2d" else "ua_attn"),
+                      ("attention_2d_3d", "ua_attn_kernel"), ("reduce", "ua_reduce_kernel")):
+        try:
+            f, n = _counter_per_launch(fetch_csv, sub, "FETCH_SIZE")
+            wv, _ = _counter_per_launch(write_csv, sub, "WRITE_SIZE")
+        except SystemExit:
+            continue
+        out["kernels"][name] = {"fetch_kib_raw": round(f, 1), "write_kib_raw": round(wv, 1),
+                                "bytes_read": round(f * 1024 * f_scale),
+                                "bytes_written": round(wv * 1024 * w_scale), "launches": n}
+    att = out["kernels"].get("attention") or out["kernels"].get("attention_2d_3d")
+    out["path"] = 3 if ("reduce" in out["kernels"]) else 2
+    out["bytes_per_launch"] = att["bytes_read"] + att["bytes_written"]
+    path = os.path.join(ROOT, "profiles", f"{args.workload}_hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, budget_s):
     """The oracle, untuned, on whole sequences drawn in a seeded order until
     about `budget_s` of wall time; reported in the metric's unit."""
@@ -95,22 +137,25 @@ def cpu_baseline(w, budget_s):
     done_bytes = done_flops = 0
     seqs = 0
     t_total = 0.0
-    for s in order:
-        lo, hi = int(w.cu_seqlens_q[s]), int(w.cu_seqlens_q[s + 1])
-        if hi == lo:
-            continue
-        rows = np.arange(lo * w.num_q_heads, hi * w.num_q_heads, dtype=np.int64)
-        t0 = time.perf_counter()
-        oracle.rows(w, rows, nthreads=threads)
-        t_total += time.perf_counter() - t0
-        sub = _subset(w, s)
-        a = algorithmic_work(sub)
-        done_bytes += a["bytes"]
-        done_flops += a["flops"]
-        seqs += 1
-        if t_total >= budget_s:
-            break
-    return dict(seconds=t_total, bytes=done_bytes, flops=done_flops, seqs=seqs, cores=threads)
+    passes = 0
+    while t_total < budget_s:
+        for s in order:
+            lo, hi = int(w.cu_seqlens_q[s]), int(w.cu_seqlens_q[s + 1])
+            if hi == lo:
+                continue
+            rows = np.arange(lo * w.num_q_heads, hi * w.num_q_heads, dtype=np.int64)
+            t0 = time.perf_counter()
+            oracle.rows(w, rows, nthreads=threads)
+            t_total += time.perf_counter() - t0
+            a = algorithmic_work(_subset(w, s))
+            done_bytes += a["bytes"]
+            done_flops += a["flops"]
+            seqs += 1
+            if t_total >= budget_s:
+                break
+        passes += 1
+    return dict(seconds=t_total, bytes=done_bytes, flops=done_flops, seqs=seqs, cores=threads,
+                passes=passes)
 
 
 def _subset(w, s):
@@ -135,7 +180,19 @@ def main():
                     help="split-KV segment length in KV tiles (0 = the plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (5 launches): the "
+                         "reference dispatch for scaling HBM traffic counters")
+    ap.add_argument("--summarize-traffic", nargs=5, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV",
+                             "COPY_BYTES"),
+                    help="write profiles/<workload>_hbm_traffic.json from rocprofv3 --pmc "
+                         "counter CSVs (no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -150,6 +207,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 16
+        src = torch.empty(n, 4, dtype=torch.int32, device="cuda").random_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 16, "copy_bytes_written": n * 16,
+                          "launches": 5}))
+        return
 
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     w = W.named(args.workload)
@@ -216,7 +285,8 @@ def main():
         cpu_value = (c["bytes"] / c["seconds"] / 1e9) if bound == "hbm" else \
             (c["flops"] / c["seconds"] / 1e12)
         cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": c["cores"], "kind": "oracle",
-               "sample": f"{c['seqs']} of {w.num_seqs} sequences (all their rows and heads), "
+               "sample": f"{c['seqs']} sequence runs over {c['passes']} pass(es) of the "
+                         f"{w.num_seqs}-sequence batch (all rows and heads of each), "
                          f"{c['seconds']:.1f} s of fp64 oracle time on {c['cores']} threads"}
 
     dtype = {0: "bf16", 1: "f16"}[w.q_dtype] + ("+fp8kv" if w.kv_dtype == 2 else "")
