@@ -765,40 +765,101 @@ __global__ __launch_bounds__(64, kMinWavesPerSimd) void ua_decode_sk_kernel(UaKe
 // The re-base of section 5 of the unified page: M = max over partials (and the
 // sink), L = sum l_i 2^(m_i - M) (+ 2^(sink - M)), O = sum o_i 2^(m_i - M) / L,
 // then the cast.  Partials with m = -inf saw no visible key and are skipped.
-// One wave per (token, query head); four per workgroup.  SK selects the
-// stream-K slot layout, else the segmented one.
+// One wave per (token, query head); four per workgroup.  Partials are merged
+// in a fixed order, four at a time with all their loads issued together, so
+// the result is the same on every run.
+template <int D, typename QT>
+__device__ __forceinline__ void merge_partials(const UaKernelParams& p, int64_t first, int64_t stride,
+                                               int count, int64_t j0, int64_t T, int64_t W, bool sk,
+                                               int tok, int head) {
+    constexpr int EPL = D / 64;  // elements per lane
+    constexpr int U = 4;
+    const int lane = threadIdx.x & 63;
+    const bool sinks = p.flags & UA_FLAG_SINKS;
+    float mx = sinks ? p.sinks[head] * kLog2e : -INFINITY;
+    float L = sinks ? 1.0f : 0.0f;  // the sink term, at its own max
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    for (int g0 = 0; g0 < count; g0 += U) {
+        float mg[U], lg[U], og[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u;
+            const int64_t j = j0 + g;
+            const bool live = g < count && (!sk || j * T / W < (j + 1) * T / W);
+            const int64_t rid = first + (int64_t)(live ? g : 0) * stride;
+            mg[u] = live ? p.ws_m[rid] : -INFINITY;
+            lg[u] = live ? p.ws_l[rid] : 0.0f;
+            const float* src = p.ws_o + rid * D + lane * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) og[u][e] = live ? src[e] : 0.0f;
+        }
+        float bm = mx;
+#pragma unroll
+        for (int u = 0; u < U; ++u) bm = fmaxf(bm, mg[u]);
+        if (bm == -INFINITY) continue;
+        const float a = fast_exp2(mx - bm);  // 0 when nothing was merged yet
+        L *= a;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] *= a;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = fast_exp2(mg[u] - bm);  // 0 for dead partials
+            L += lg[u] * w;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] += w * og[u][e];
+        }
+        mx = bm;
+    }
+    const float inv = L > 0.0f ? p.out_scale / L : 0.0f;
+    QT* dst = reinterpret_cast<QT*>(p.o) + (int64_t)tok * p.o_stride_tok + (int64_t)head * D +
+              lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = (QT)(acc[e] * inv);
+}
+
 template <int D, typename QT, bool SK>
 __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_t n_rows) {
-    constexpr int EPL = D / 64;  // elements per lane
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= n_rows) return;
     const int tok = (int)(row / p.num_q_heads);
     const int head = (int)(row - (int64_t)tok * p.num_q_heads);
-    const int s = token_seq(p.cu_q, p.num_seqs, tok);
-    const int q_start = p.cu_q[s];
-    const int q_len = p.cu_q[s + 1] - q_start;
 
-    // partials of this row: workspace rows first + g * stride for g < count;
-    // stream-K skips workers whose flattened range is empty
-    int64_t first, stride;
-    int count;
-    int64_t T = 0, W = 1;
-    int j0 = 0;
     if (SK) {
-        int n, total;
-        const int xs = sk_seq_prefix<kSkTile>(p, s, &n, &total);
+        // one pass over the sequences: the token's sequence s, the first
+        // flattened tile of s, its tile count and the total T
+        int carry = 0, s = -1, xs = 0, n = 0, q_start = 0;
+        for (int base = 0; base < p.num_seqs; base += 64) {
+            const SeqLane q = seq_lane<kSkTile>(p, base + lane);
+            const int v = q.n * p.num_kv_heads;
+            const int incl = wave_incl_scan(v);
+            const bool past = base + lane < p.num_seqs && q.q_start + q.q_len <= tok;
+            const uint64_t before = __ballot(!past && base + lane < p.num_seqs);
+            if (s < 0 && before) {
+                const int l = __builtin_ctzll(before);
+                s = base + l;
+                xs = carry + readlane(incl - v, l);
+                n = readlane(q.n, l);
+                q_start = readlane(q.q_start, l);
+            }
+            carry += readlane(incl, 63);
+        }
+        const int64_t T = carry;
+        const int64_t W = p.sk_workers;
         const int hk = head / p.group;
         const int64_t x0 = xs + (int64_t)hk * n;
-        T = total;
-        W = p.sk_workers;
-        j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
+        const int j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
         const int j1 = T > 0 ? sk_worker_of(x0 + n - 1, T, W) : 0;
         const int r = (tok - q_start) * p.group + (head - hk * p.group);
-        first = ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r;
-        stride = p.rows_used;
-        count = (n > 0 && T > 0) ? j1 - j0 + 1 : 0;
+        const int count = (s >= 0 && n > 0 && T > 0) ? j1 - j0 + 1 : 0;
+        merge_partials<D, QT>(p, ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r,
+                              p.rows_used, count, j0, T, W, true, tok, head);
     } else {
+        const int s = token_seq(p.cu_q, p.num_seqs, tok);
+        const int q_start = p.cu_q[s];
+        const int q_len = p.cu_q[s + 1] - q_start;
         const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
         const int ctx = s_k - q_len;
         const int p0 = ((tok - q_start) / p.block_q) * p.block_q;
@@ -806,43 +867,11 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const KeyRange kr = key_range(p.flags, p.window, s_k, ctx, p0, p_last);
         const int t_lo = kr.lo / p.tile_n;
         const int t_hi = (kr.hi + p.tile_n - 1) / p.tile_n;
-        first = row * p.num_segments;
-        stride = 1;
-        count = t_hi > t_lo ? min(p.num_segments, (t_hi - t_lo + p.tiles_per_seg - 1) /
-                                                      p.tiles_per_seg)
-                            : 0;
+        const int count = t_hi > t_lo ? min(p.num_segments, (t_hi - t_lo + p.tiles_per_seg - 1) /
+                                                                p.tiles_per_seg)
+                                      : 0;
+        merge_partials<D, QT>(p, row * p.num_segments, 1, count, 0, 1, 1, false, tok, head);
     }
-    auto live = [&](int g) {
-        if (!SK) return true;
-        const int64_t j = j0 + g;
-        return j * T / W < (j + 1) * T / W;
-    };
-
-    const bool sinks = p.flags & UA_FLAG_SINKS;
-    const float sink2 = sinks ? p.sinks[head] * kLog2e : -INFINITY;
-    float mx = sink2;
-    for (int g = 0; g < count; ++g)
-        if (live(g)) mx = fmaxf(mx, p.ws_m[first + g * stride]);
-    float L = sinks ? fast_exp2(sink2 - mx) : 0.0f;
-    float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-    for (int g = 0; g < count; ++g) {
-        if (!live(g)) continue;
-        const int64_t rid = first + g * stride;
-        const float mg = p.ws_m[rid];
-        if (mg == -INFINITY) continue;
-        const float w = fast_exp2(mg - mx);
-        L += p.ws_l[rid] * w;
-        const float* src = p.ws_o + rid * D + lane * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
-    }
-    const float inv = L > 0.0f ? p.out_scale / L : 0.0f;
-    QT* dst = reinterpret_cast<QT*>(p.o) + (int64_t)tok * p.o_stride_tok + (int64_t)head * D +
-              lane * EPL;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = (QT)(acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
