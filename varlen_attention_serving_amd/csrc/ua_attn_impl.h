@@ -73,6 +73,10 @@ constexpr int kVPad = 32;  // V LDS row padding (elements)
 #define UA_MIN_WAVES_PER_SIMD 2
 #endif
 constexpr int kMinWavesPerSimd = UA_MIN_WAVES_PER_SIMD;
+// four-wave workgroups with d <= 128: three resident per CU (168 VGPRs per lane)
+constexpr int kMinWavesPerSimdWide = 3;
+// log2-unit slack before the running reference max is moved (p <= 2^8)
+constexpr float kLazyRescale = 8.0f;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -105,7 +109,12 @@ template <> struct QType<_Float16> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// the value of lane l ^ 32 (one v_permlane32_swap, no LDS round trip)
+__device__ __forceinline__ float xor32(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // tanh(y) = sign(y) (1 - e^{-2|y|}) / (1 + e^{-2|y|}), with e^z via 2^(z log2 e)
 __device__ __forceinline__ float tanh_f32(float y) {
@@ -334,33 +343,51 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
     const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
     const float c = XFORM ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-            float sv = sacc[kt][i];
-            if (XFORM) {
-                sv = softcap ? p.softcap_out * tanh_f32(sv * p.softcap_in) : sv * p.qk_scale_log2;
-                sv = alibi ? sv + rc.slope2 * (float)(key - rc.ctx) : sv;
-            }
-            sv = (need_mask && (key < rc.kmin || key > rc.kmax)) ? -INFINITY : sv;
-            sacc[kt][i] = sv;
-            mt = fmaxf(mt, sv);
+    auto transform = [&](float x, int key) {
+        if (XFORM) {
+            x = softcap ? p.softcap_out * tanh_f32(x * p.softcap_in) : x * p.qk_scale_log2;
+            x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
         }
+        return x;
+    };
+    if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+                const bool keep = (key >= rc.kmin) & (key <= rc.kmax);
+                const float sv = keep ? transform(sacc[kt][i], key) : -INFINITY;
+                sacc[kt][i] = sv;
+                mt = fmaxf(mt, sv);
+            }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+                const float sv = transform(sacc[kt][i], key);
+                sacc[kt][i] = sv;
+                mt = fmaxf(mt, sv);
+            }
     }
     mt = fmaxf(mt, xor32(mt)) * c;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    // O and l are re-based only when some row's max moved: elsewhere alpha is
-    // exactly 1, so skipping the multiply changes nothing.
-    if (__ballot(m_new != m_run)) {
-        const float alpha = fast_exp2(m_run - m_use);
+    // Lazy reference max: exponents are taken against m_run, which moves only
+    // when some row's tile max exceeds it by more than kLazyRescale (log2
+    // units).  Softmax is shift-invariant, so o and l stay exact relative to
+    // m_run; between moves p <= 2^kLazyRescale.  A move re-bases O and l by
+    // 2^(m_old - m_new).
+    if (__ballot(mt > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float m_base = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_base);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
     }
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
@@ -420,7 +447,7 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // ---------------------------------------------------------------------------
 
 template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, bool XFORM>
-__global__ __launch_bounds__(NW * 64, kMinWavesPerSimd) void ua_attn_kernel(UaKernelParams p) {
+__global__ __launch_bounds__(NW * 64, (NW >= 4 && D <= 128) ? kMinWavesPerSimdWide : kMinWavesPerSimd) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, NW, BN, FP8> G;
