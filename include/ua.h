@@ -108,7 +108,9 @@ typedef struct ua_problem* ua_problem_t;
  *  timing_events  optional hipEvent_t handles (NULL to skip each): [0] is
  *               recorded on the stream before the attention kernel, [1] after
  *               it (before the split-KV reduce, if any), [2] after the last
- *               kernel, so a caller can time the kernels one by one.
+ *               kernel, so a caller can time the kernels one by one.  On a
+ *               class-split run (ua_plan_info.class_split) [0] precedes both
+ *               launches and [1], [2] follow both, reduces included.
  * Device metadata is trusted: 0 <= q_len <= S_k <= max_seqlen_k, and used
  * block-table entries lie in [0, num_blocks). */
 typedef struct ua_run_args {
@@ -141,11 +143,15 @@ typedef struct ua_plan_info {
     int32_t tile_n;          /* keys per KV tile */
     int32_t waves;           /* wave64s per workgroup */
     int32_t num_segments;    /* split-KV segments per q-block (1 on the 2D path) */
-    int32_t tiles_per_segment;
+    int32_t tiles_per_segment; /* a q-block with n live tiles is cut into
+                                min(num_segments, ceil(n / tiles_per_segment))
+                                near-equal runs (segmented split path) */
     int32_t grid[3];         /* launch grid of the attention kernel */
     int32_t use_i64_kv;      /* 1 when the KV pool exceeds 2^31 bytes */
-    int32_t stream_k;        /* 1 when the split path balances KV tiles over resident
-                                workers (decode-shaped batches), 0 for fixed segments */
+    int32_t stream_k;        /* 1 when single-wave (decode-shaped) rows take the split
+                                path with KV tiles balanced over resident workers */
+    int32_t class_split;     /* 1 when a wide batch's decode-shaped sequences run in a
+                                stream-K launch and the rest in the launch described above */
 } ua_plan_info_t;
 
 /* Validate a description and build a problem handle (host only; no device
@@ -162,7 +168,12 @@ ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_
                           int32_t max_seqlen_q, int32_t max_seqlen_k, ua_plan_info_t* info);
 
 /* Enqueue one forward pass on `stream` (asynchronous; nothing is read back to
- * the host).  Validation errors return before anything is enqueued. */
+ * the host).  Validation errors return before anything is enqueued.  A
+ * class-split run forks its stream-K launch onto a stream the handle owns
+ * (created, at default priority, on the first such run; the handle then stays
+ * on that device) and joins it back into `stream` before returning, so work
+ * enqueued on `stream` afterwards sees the whole output.  A handle serves one
+ * host thread at a time. */
 ua_status_t ua_run(ua_problem_t problem, const ua_run_args_t* args, void* stream);
 
 /* Release a handle (NULL is ignored). */

@@ -35,7 +35,7 @@ def _full_check(w, force="auto", what=None):
     say(f"[gpu] {what}: T_q={w.total_q} H={w.num_q_heads}/{w.num_kv_heads} d={w.head_dim} "
         f"b={w.block_size}")
     o, plan = run_hip(w, FORCE[force], split_segment_tiles=SEG_TILES.get(force, 0))
-    say(f"  plan path={plan.path} stream_k={plan.stream_k} waves={plan.waves} "
+    say(f"  plan path={plan.path} split={plan.class_split} stream_k={plan.stream_k} waves={plan.waves} "
         f"tile_n={plan.tile_n} segments={plan.num_segments} tps={plan.tiles_per_segment} "
         f"grid={list(plan.grid)}")
     if force == "2d":
@@ -113,6 +113,34 @@ def test_stream_k_ragged_decode(seed, hk):
                 use_alibi=seed == 2, softcap=30.0 if seed == 2 else 0.0)
     _, plan = _full_check(w, "3d")
     assert plan.stream_k == 1
+
+
+MIXED = [
+    ("plain", dict(), (32, 8, 128, 16)),
+    ("window_softcap", dict(window=300, softcap=30.0), (32, 8, 128, 32)),
+    ("fp8_alibi_sinks_window", dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True,
+                                    use_sinks=True, window=200), (16, 2, 256, 64)),
+    ("d64_g2", dict(use_sinks=True), (8, 4, 64, 16)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MIXED)))
+def test_mixed_decode_and_chunks(i):
+    """Decode rows and multi-row chunks in one batch: the decode-shaped
+    sequences run in the stream-K launch, the rest in the wide launch."""
+    name, flags, (hq, hk, d, b) = MIXED[i]
+    rng = np.random.default_rng(400 + i)
+    n_dec, n_chunk = 9, 3
+    dec_k = rng.integers(1, 900, size=n_dec, endpoint=True)
+    ctx = rng.integers(0, 600, size=n_chunk, endpoint=True)
+    ch_q = rng.integers(40, 200, size=n_chunk, endpoint=True)
+    q_lens = np.concatenate([np.ones(n_dec, np.int64), ch_q])
+    sk = np.concatenate([dec_k, ctx + ch_q])
+    order = rng.permutation(q_lens.size)
+    w = W.build(f"mixed_{name}", 400 + i, q_lens[order], sk[order], num_q_heads=hq,
+                num_kv_heads=hk, head_dim=d, block_size=b, rng=rng, **flags)
+    _, plan = _full_check(w, "auto")
+    assert plan.class_split == 1
 
 
 @pytest.mark.parametrize("force", ["auto", "2d", "3d"])

@@ -96,6 +96,7 @@ class ua_plan_info_t(ctypes.Structure):
         ("grid", ctypes.c_int32 * 3),
         ("use_i64_kv", ctypes.c_int32),
         ("stream_k", ctypes.c_int32),
+        ("class_split", ctypes.c_int32),
     ]
 
 

@@ -2,10 +2,12 @@
 //
 // The plan follows "Unified paged attention on gfx950, from the math up",
 // section 6: the 2D query-tile kernel when the q-block x kv-head grid already
-// fills the device (at least 4 workgroups per compute unit), when the
-// context is short (S_k <= 512) or under a sliding window; otherwise the 3D
-// split-KV kernel plus its log-sum-exp reduce.  Everything is decided from
-// host values (no device reads, no synchronisation).
+// fills the device (at least 4 workgroups per compute unit) or when a q-block
+// visits few keys (a short context or a short sliding window); otherwise the
+// 3D split-KV kernel plus its log-sum-exp reduce.  In a batch of wide
+// q-blocks the decode-shaped sequences go to a stream-K launch that runs
+// beside the wide one.  Everything is decided from host values (no device
+// reads, no synchronisation).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -23,6 +25,8 @@ namespace {
 constexpr int kNumCUs = 256;            // MI355X compute units
 constexpr int kMinTilesPerSegment = 4;  // keep each split segment worth its partials
 constexpr int kSplitTargetWorkgroups = 8 * kNumCUs;
+constexpr int kWideResidentPerCU = 3;   // four-wave workgroups resident per CU
+constexpr int kMaxWideSegments = 2;
 constexpr size_t kWorkspaceCap = size_t(2) << 30;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -50,98 +54,175 @@ struct ua_problem {
     int log2_block;
     bool fp8;
     size_t ws_bytes;
+    // a split batch runs its stream-K launch on a second stream, forked from
+    // and joined back into the caller's (created on the first split run)
+    int side_device = -1;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    ~ua_problem() {
+        if (side) (void)hipStreamDestroy(side);
+        if (fork) (void)hipEventDestroy(fork);
+        if (join) (void)hipEventDestroy(join);
+    }
 };
 
 namespace {
 
 int row_bytes(const ua_problem& P) { return (P.d.head_dim + 2) * 4; }
 
-struct Plan {
-    int path, waves, tile_n, block_m, block_q, num_segments, tiles_per_seg, stream_k;
+// One kernel launch of the plan (plus its reduce on the split path).
+struct Sub {
+    int path;          // 2 = query-tile kernel, 3 = split-KV kernel + reduce
+    int stream_k;      // split path: balanced workers (single-wave geometry)
+    int waves, tile_n, block_m, block_q, num_segments, tiles_per_seg;
+    int class_mode;    // 0 all sequences, 1 single-wave ones only, 2 the others
     int64_t slots;
     unsigned grid[3];
 };
 
+struct Plan {
+    int n;             // 1, or 2 when decode rows of a wide batch go to stream-K
+    Sub sub[2];        // sub[n - 1] holds the rows of the widest geometry
+    int small_block_q; // positions of a single-wave q-block (32 / g, 0 if g > 32)
+};
+
 // stream-K partial slots: one per (sequence, kv-head) pair plus one per worker
 size_t stream_k_bytes(const ua_problem& P, int64_t num_seqs, int rows_per_slot) {
-    return (size_t)(num_seqs * P.d.num_kv_heads + kMaxStreamKWorkers) * rows_per_slot *
-           (size_t)row_bytes(P);
+    const size_t b = (size_t)(num_seqs * P.d.num_kv_heads + kMaxStreamKWorkers) * rows_per_slot *
+                     (size_t)row_bytes(P);
+    return (b + 255) & ~size_t(255);
+}
+
+void geometry(const ua_problem& P, int waves, Sub* g) {
+    const ua_problem_desc_t& d = P.d;
+    g->waves = waves;
+    g->tile_n = 32;
+    // a tile must hold whole passes of the workgroup's 16-byte row chunks
+    const int chunks_per_row = d.head_dim * (P.fp8 ? 1 : 2) / 16;
+    g->tile_n = std::max(g->tile_n, waves * 64 / chunks_per_row);
+    g->block_m = 32 * waves;
+    g->block_q = g->block_m / P.group;
+}
+
+// The segmented split: grid z holds the segments; each q-block cuts its own
+// live tile range into up to that many near-equal runs of about
+// tiles_per_seg tiles (the kernel and the reduce agree on the cut).
+ua_status_t segmented(const ua_problem& P, int64_t total_q, int64_t live_blocks, int64_t span,
+                      size_t ws_cap, Sub* g) {
+    const ua_problem_desc_t& d = P.d;
+    g->path = 3;
+    const int64_t max_tiles = std::max<int64_t>(1, cdiv(std::max<int64_t>(span, 1), g->tile_n) + 1);
+    // expected live tiles (ragged lengths: about half of the maximum) over
+    // the workgroups we want resident
+    const int64_t work = std::max<int64_t>(1, d.num_kv_heads * live_blocks * max_tiles / 2);
+    int64_t tps = std::max<int64_t>(kMinTilesPerSegment, cdiv(work, kSplitTargetWorkgroups));
+    int64_t ns = 0;
+    if (g->waves > 1 && d.split_segment_tiles == 0) {
+        // about two resident rounds of wide workgroups: each q-block cuts its
+        // own tile range into up to ns runs of at least kMinTilesPerSegment
+        const int64_t grid = std::max<int64_t>(1, d.num_kv_heads * (total_q / g->block_q + 1));
+        ns = std::min<int64_t>(kMaxWideSegments, cdiv(2 * kWideResidentPerCU * kNumCUs, grid));
+        tps = kMinTilesPerSegment;
+        ns = std::max<int64_t>(1, std::min(ns, cdiv(max_tiles, tps)));
+    } else {
+        if (d.split_segment_tiles > 0) tps = d.split_segment_tiles;
+        tps = std::min(tps, max_tiles);
+        ns = cdiv(max_tiles, tps);
+    }
+    const int64_t rows = std::max<int64_t>(1, total_q * d.num_q_heads);
+    const int64_t cap = (int64_t)(ws_cap / ((size_t)rows * row_bytes(P)));
+    if (cap < 1) return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
+    if (ns > cap) {
+        tps = cdiv(max_tiles, cap);
+        ns = cdiv(max_tiles, tps);
+    }
+    g->num_segments = (int)ns;
+    g->tiles_per_seg = (int)tps;
+    g->grid[0] = (unsigned)g->slots;
+    g->grid[1] = d.num_kv_heads;
+    g->grid[2] = (unsigned)ns;
+    return UA_OK;
 }
 
 ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, int32_t max_q,
                       int32_t max_k, Plan* out) {
     const ua_problem_desc_t& d = P.d;
     Plan pl{};
-    // geometry: one wave of 32 rows when the rows of any q-block fit in it
-    // (decode-like batches), else four waves (128 rows) sharing each KV tile;
-    // 32-key tiles keep every variant at three or more waves per SIMD
+    pl.small_block_q = P.group <= 32 ? 32 / P.group : 0;
+    const bool force2 = d.flags & UA_FLAG_FORCE_2D;
+    const bool force3 = d.flags & UA_FLAG_FORCE_3D;
+    // Keys one q-block can visit.  The shape rule of section 6 of the unified
+    // page keeps short contexts and sliding windows on the query-tile path
+    // because they leave a q-block only a few KV tiles; the span states that
+    // directly (a window of thousands of keys is not short).
+    const int64_t span = (d.flags & UA_FLAG_WINDOW)
+                             ? std::min<int64_t>(max_k, (int64_t)d.window + std::max(max_q, 1))
+                             : max_k;
+    // geometry: one wave of 32 rows when every q-block fits in it (decode-like
+    // batches), else four waves (128 rows) sharing each KV tile
     const bool small = (int64_t)std::max(max_q, 1) * P.group <= 32;
-#if defined(UA_EXPERIMENT_WIDE)
-    pl.waves = small ? 1 : UA_WIDE_WAVES;
-    pl.tile_n = small ? 32 : (d.head_dim >= 256 ? 32 : UA_WIDE_TILE_N);
-#else
-    pl.waves = small ? 1 : 4;
-    pl.tile_n = 32;
-#endif
-    {
-        // a tile must hold whole passes of the workgroup's 16-byte row chunks
-        const int chunks_per_row = d.head_dim * (P.fp8 ? 1 : 2) / 16;
-        const int rows_per_pass = pl.waves * 64 / chunks_per_row;
-        pl.tile_n = std::max(pl.tile_n, rows_per_pass);
+    const int64_t sk_tiles = (int64_t)num_seqs * d.num_kv_heads * (cdiv(std::max<int64_t>(span, 1), kSkTile) + 2);
+    const bool sk_fits = sk_tiles < INT32_MAX;
+
+    Sub& w = pl.sub[0];
+    geometry(P, small ? 1 : 4, &w);
+    w.slots = total_q / w.block_q + num_seqs;
+    if (w.slots > INT32_MAX / 2) return fail(UA_ERR_UNSUPPORTED, "too many query blocks");
+    // q-blocks that carry rows (at most one partial block per sequence)
+    const int64_t live_blocks = std::min<int64_t>(w.slots, num_seqs + total_q / w.block_q);
+    bool two_d = (int64_t)d.num_kv_heads * w.slots >= 4 * kNumCUs || span <= 512;
+    if (!small && !two_d) {
+        // Wide q-blocks carry 128 fp32 rows of partials per segment, so split
+        // them only when the query-tile grid is short of one resident round
+        // (three four-wave workgroups per CU), and only as far as needed.
+        const int64_t wide_grid = (int64_t)d.num_kv_heads * (total_q / w.block_q + 1);
+        two_d = wide_grid >= kWideResidentPerCU * kNumCUs;
     }
-    pl.block_m = 32 * pl.waves;
-    pl.block_q = pl.block_m / P.group;
-    pl.slots = total_q / pl.block_q + num_seqs;
-    if (pl.slots > INT32_MAX / 2) return fail(UA_ERR_UNSUPPORTED, "too many query blocks");
+    if (force2) two_d = true;
+    if (force3) two_d = false;
 
-    const bool window = d.flags & UA_FLAG_WINDOW;
-    bool two_d = (int64_t)d.num_kv_heads * pl.slots >= 4 * kNumCUs || max_k <= 512 || window;
-    if (d.flags & UA_FLAG_FORCE_2D) two_d = true;
-    if (d.flags & UA_FLAG_FORCE_3D) two_d = false;
-
+    // decode rows of a wide batch go to the stream-K kernel, the rest here
+    const bool split = !small && !force2 && !force3 && pl.small_block_q > 0 && sk_fits &&
+                       d.split_segment_tiles == 0;
+    w.class_mode = split ? 2 : 0;
+    size_t ws_seg = P.ws_bytes;
+    if (split) {
+        Sub& k = pl.sub[0];
+        Sub wide = w;
+        geometry(P, 1, &k);
+        k.slots = num_seqs;
+        k.path = 3;
+        k.stream_k = 1;
+        k.class_mode = 1;
+        k.grid[0] = 0;
+        k.grid[1] = k.grid[2] = 1;
+        const size_t skb = stream_k_bytes(P, num_seqs, k.block_q * P.group);
+        if (skb > P.ws_bytes) return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
+        ws_seg = P.ws_bytes - skb;
+        pl.sub[1] = wide;
+        pl.n = 2;
+    } else {
+        pl.n = 1;
+    }
+    Sub& g = pl.sub[pl.n - 1];
     if (two_d) {
-        pl.path = 2;
-        pl.num_segments = 1;
-        pl.tiles_per_seg = 0;
-        pl.grid[0] = d.num_kv_heads;
-        pl.grid[1] = (unsigned)pl.slots;
-        pl.grid[2] = 1;
-    } else if (small && d.split_segment_tiles == 0 &&
-               (int64_t)num_seqs * d.num_kv_heads * (cdiv(std::max(max_k, 1), kSkTile) + 1) <
-                   INT32_MAX) {
+        g.path = 2;
+        g.num_segments = 1;
+        g.tiles_per_seg = 0;
+        g.grid[0] = d.num_kv_heads;
+        g.grid[1] = (unsigned)g.slots;
+        g.grid[2] = 1;
+    } else if (small && d.split_segment_tiles == 0 && sk_fits) {
         // every sequence's rows fit one q-block: balance KV tiles over workers
-        pl.path = 3;
-        pl.stream_k = 1;
-        pl.num_segments = 0;
-        pl.tiles_per_seg = 0;
-        pl.grid[0] = 0;  // resident worker count, fixed at launch
-        pl.grid[1] = 1;
-        pl.grid[2] = 1;
-        if (stream_k_bytes(P, num_seqs, pl.block_q * P.group) > P.ws_bytes)
+        g.path = 3;
+        g.stream_k = 1;
+        g.grid[0] = 0;  // resident worker count, fixed at launch
+        g.grid[1] = g.grid[2] = 1;
+        if (stream_k_bytes(P, num_seqs, g.block_q * P.group) > P.ws_bytes)
             return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
     } else {
-        pl.path = 3;
-        const int64_t max_tiles = std::max<int64_t>(1, cdiv(std::max(max_k, 1), pl.tile_n));
-        // expected live tiles (ragged lengths: about half of the maximum) over
-        // the workgroups we want resident
-        const int64_t live_blocks = std::min<int64_t>(pl.slots, num_seqs + total_q / pl.block_q);
-        const int64_t work = std::max<int64_t>(1, d.num_kv_heads * live_blocks * max_tiles / 2);
-        int64_t tps = std::max<int64_t>(kMinTilesPerSegment, cdiv(work, kSplitTargetWorkgroups));
-        if (d.split_segment_tiles > 0) tps = d.split_segment_tiles;
-        tps = std::min(tps, max_tiles);
-        int64_t ns = cdiv(max_tiles, tps);
-        const int64_t rows = std::max<int64_t>(1, total_q * d.num_q_heads);
-        const int64_t cap = (int64_t)(P.ws_bytes / ((size_t)rows * row_bytes(P)));
-        if (cap < 1) return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
-        if (ns > cap) {
-            tps = cdiv(max_tiles, cap);
-            ns = cdiv(max_tiles, tps);
-        }
-        pl.num_segments = (int)ns;
-        pl.tiles_per_seg = (int)tps;
-        pl.grid[0] = (unsigned)pl.slots;
-        pl.grid[1] = d.num_kv_heads;
-        pl.grid[2] = (unsigned)ns;
+        ua_status_t st = segmented(P, total_q, live_blocks, span, ws_seg, &g);
+        if (st != UA_OK) return st;
     }
     *out = pl;
     return UA_OK;
@@ -220,9 +301,10 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     const int64_t ns_max =
         std::max<int64_t>(1, cdiv(cdiv(std::max(d.max_seqlen_k, 1), 32), min_tps));
     const int64_t ns_cap = std::max<int64_t>(1, (int64_t)(kWorkspaceCap / per_seg));
-    P->ws_bytes = per_seg * (size_t)std::min(ns_max, ns_cap);
-    // the stream-K split (single-wave geometry, 32 rows per q-block)
-    P->ws_bytes = std::max(P->ws_bytes, stream_k_bytes(*P, std::max(d.max_num_seqs, 1), 32));
+    // the segmented split region, then the stream-K region (single-wave
+    // geometry, at most 32 rows per q-block)
+    P->ws_bytes = ((per_seg * (size_t)std::min(ns_max, ns_cap) + 255) & ~size_t(255)) +
+                  stream_k_bytes(*P, std::max(d.max_num_seqs, 1), 32);
     *out = P;
     return UA_OK;
 }
@@ -242,16 +324,18 @@ ua_status_t ua_query_plan(ua_problem_t p, int32_t num_seqs, int64_t total_q, int
     Plan pl;
     ua_status_t st = make_plan(*p, num_seqs, total_q, max_seqlen_q, max_seqlen_k, &pl);
     if (st != UA_OK) return st;
-    info->path = pl.path;
-    info->block_m = pl.block_m;
-    info->block_q = pl.block_q;
-    info->tile_n = pl.tile_n;
-    info->waves = pl.waves;
-    info->num_segments = pl.num_segments;
-    info->tiles_per_segment = pl.tiles_per_seg;
-    for (int i = 0; i < 3; ++i) info->grid[i] = (int32_t)pl.grid[i];
+    const Sub& g = pl.sub[pl.n - 1];  // the launch holding the widest rows
+    info->path = g.path;
+    info->block_m = g.block_m;
+    info->block_q = g.block_q;
+    info->tile_n = g.tile_n;
+    info->waves = g.waves;
+    info->num_segments = g.num_segments;
+    info->tiles_per_segment = g.tiles_per_seg;
+    for (int i = 0; i < 3; ++i) info->grid[i] = (int32_t)g.grid[i];
     const int esz = p->fp8 ? 1 : 2;
-    info->stream_k = pl.stream_k;
+    info->stream_k = pl.sub[0].stream_k;
+    info->class_split = pl.n == 2;
     info->use_i64_kv =
         (double)p->d.num_blocks * p->d.block_size * p->d.num_kv_heads * p->d.head_dim * esz >
         2147483648.0;
@@ -298,86 +382,147 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     ua_status_t st = make_plan(*p, a->num_seqs, a->total_q, a->max_seqlen_q, a->max_seqlen_k, &pl);
     if (st != UA_OK) return st;
 
-    UaKernelParams kp{};
-    kp.q = a->q;
-    kp.k = a->k_cache;
-    kp.v = a->v_cache;
-    kp.o = a->o;
-    kp.block_table = a->block_table;
-    kp.seq_lens = a->seq_lens;
-    kp.cu_q = a->cu_seqlens_q;
-    kp.slopes = (d.flags & UA_FLAG_ALIBI) ? a->alibi_slopes : nullptr;
-    kp.sinks = (d.flags & UA_FLAG_SINKS) ? a->sinks : nullptr;
-    kp.q_stride_tok = a->q_stride_tok;
-    kp.o_stride_tok = a->o_stride_tok;
-    kp.kv_slot_stride = (int64_t)d.num_kv_heads * d.head_dim;
-    kp.num_seqs = a->num_seqs;
-    kp.num_q_heads = d.num_q_heads;
-    kp.num_kv_heads = d.num_kv_heads;
-    kp.group = p->group;
-    kp.block_size_log2 = p->log2_block;
-    kp.bt_stride = a->block_table_stride;
-    kp.block_q = pl.block_q;
-    kp.rows_used = pl.block_q * p->group;
-    kp.tile_n = pl.tile_n;
-    kp.tiles_per_seg = pl.tiles_per_seg;
-    kp.num_segments = pl.num_segments;
-    kp.flags = d.flags;
-    kp.window = (d.flags & UA_FLAG_WINDOW) ? d.window : 0;
+    UaKernelParams base{};
+    base.q = a->q;
+    base.k = a->k_cache;
+    base.v = a->v_cache;
+    base.o = a->o;
+    base.block_table = a->block_table;
+    base.seq_lens = a->seq_lens;
+    base.cu_q = a->cu_seqlens_q;
+    base.slopes = (d.flags & UA_FLAG_ALIBI) ? a->alibi_slopes : nullptr;
+    base.sinks = (d.flags & UA_FLAG_SINKS) ? a->sinks : nullptr;
+    base.q_stride_tok = a->q_stride_tok;
+    base.o_stride_tok = a->o_stride_tok;
+    base.kv_slot_stride = (int64_t)d.num_kv_heads * d.head_dim;
+    base.num_seqs = a->num_seqs;
+    base.num_q_heads = d.num_q_heads;
+    base.num_kv_heads = d.num_kv_heads;
+    base.group = p->group;
+    base.block_size_log2 = p->log2_block;
+    base.bt_stride = a->block_table_stride;
+    base.flags = d.flags;
+    base.window = (d.flags & UA_FLAG_WINDOW) ? d.window : 0;
     const float kscale = p->fp8 ? d.k_scale : 1.0f;
-    kp.qk_scale_log2 = d.scale * kscale * kLog2e;
-    kp.softcap_in = (d.flags & UA_FLAG_SOFTCAP) ? d.scale * kscale / d.softcap : 0.0f;
-    kp.softcap_out = (d.flags & UA_FLAG_SOFTCAP) ? d.softcap * kLog2e : 0.0f;
-    kp.out_scale = p->fp8 ? d.v_scale : 1.0f;
+    base.qk_scale_log2 = d.scale * kscale * kLog2e;
+    base.softcap_in = (d.flags & UA_FLAG_SOFTCAP) ? d.scale * kscale / d.softcap : 0.0f;
+    base.softcap_in2 = 2.0f * kLog2e * base.softcap_in;
+    base.softcap_out = (d.flags & UA_FLAG_SOFTCAP) ? d.softcap * kLog2e : 0.0f;
+    base.out_scale = p->fp8 ? d.v_scale : 1.0f;
+    base.small_block_q = pl.small_block_q;
 
-    if (pl.path == 3 && pl.stream_k) {
-        const int rows_per_slot = pl.block_q * p->group;
-        const size_t slots = (size_t)a->num_seqs * d.num_kv_heads + kMaxStreamKWorkers;
-        const size_t need = stream_k_bytes(*p, a->num_seqs, rows_per_slot);
-        if (!a->workspace || a->workspace_bytes < need)
-            return fail(UA_ERR_WORKSPACE, "split path needs %zu workspace bytes, got %zu", need,
-                        a->workspace ? a->workspace_bytes : (size_t)0);
-        if ((uintptr_t)a->workspace & 255)
-            return fail(UA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-        float* ws = static_cast<float*>(a->workspace);
-        const size_t rows = slots * rows_per_slot;
-        kp.ws_o = ws;
-        kp.ws_m = ws + rows * d.head_dim;
-        kp.ws_l = kp.ws_m + rows;
-    } else if (pl.path == 3) {
-        const size_t rows = (size_t)a->total_q * d.num_q_heads;
-        const size_t need = rows * (size_t)pl.num_segments * row_bytes(*p);
-        if (!a->workspace || a->workspace_bytes < need)
-            return fail(UA_ERR_WORKSPACE, "split path needs %zu workspace bytes, got %zu", need,
-                        a->workspace ? a->workspace_bytes : (size_t)0);
-        if ((uintptr_t)a->workspace & 255)
-            return fail(UA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-        float* ws = static_cast<float*>(a->workspace);
-        kp.ws_o = ws;
-        kp.ws_m = ws + rows * pl.num_segments * d.head_dim;
-        kp.ws_l = kp.ws_m + rows * pl.num_segments;
+    // workspace: [segmented partials][stream-K partials], both 256-byte aligned
+    if (a->workspace && ((uintptr_t)a->workspace & 255))
+        return fail(UA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    size_t need = 0;
+    size_t seg_bytes = 0, sk_bytes = 0;
+    for (int i = 0; i < pl.n; ++i) {
+        const Sub& g = pl.sub[i];
+        if (g.path == 3 && g.stream_k)
+            sk_bytes = stream_k_bytes(*p, a->num_seqs, g.block_q * p->group);
+        else if (g.path == 3)
+            seg_bytes = ((size_t)a->total_q * d.num_q_heads * g.num_segments * row_bytes(*p) + 255) &
+                        ~size_t(255);
     }
-
-    UaLaunch l{};
-    l.path = pl.path;
-    l.waves = pl.waves;
-    l.tile_n = pl.tile_n;
-    l.head_dim = d.head_dim;
-    l.q_dtype = d.q_dtype;
-    l.kv_fp8 = p->fp8;
-    for (int i = 0; i < 3; ++i) l.grid[i] = pl.grid[i];
-    l.stream_k = pl.stream_k;
-    l.reduce_rows = a->total_q * d.num_q_heads;
-    for (int i = 0; i < 3; ++i) l.events[i] = static_cast<hipEvent_t>(a->timing_events[i]);
+    need = seg_bytes + sk_bytes;
+    if (need && (!a->workspace || a->workspace_bytes < need))
+        return fail(UA_ERR_WORKSPACE, "split path needs %zu workspace bytes, got %zu", need,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    switch (d.head_dim) {
-        case 64: e = ua_launch_d64(kp, l, s); break;
-        case 128: e = ua_launch_d128(kp, l, s); break;
-        default: e = ua_launch_d256(kp, l, s); break;
+    hipEvent_t* tev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->timing_events));
+    if (pl.n == 2) {
+        // The two launches share no data until the output: fork the stream-K
+        // (HBM-bound) launch onto the side stream so it fills the compute
+        // units the wide (MFMA-bound) launch leaves free.
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(UA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (!p->side) {
+            hipStream_t side = nullptr;
+            hipEvent_t fork = nullptr, join = nullptr;
+            if ((e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking)) == hipSuccess &&
+                (e = hipEventCreateWithFlags(&fork, hipEventDisableTiming)) == hipSuccess)
+                e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                if (side) (void)hipStreamDestroy(side);
+                if (fork) (void)hipEventDestroy(fork);
+                return fail(UA_ERR_HIP, "side stream set-up: %s", hipGetErrorString(e));
+            }
+            p->side = side;
+            p->fork = fork;
+            p->join = join;
+            p->side_device = dev;
+        } else if (p->side_device != dev) {
+            return fail(UA_ERR_UNSUPPORTED,
+                        "split batches of one problem run on one device (%d, now %d)",
+                        p->side_device, dev);
+        }
+        if ((tev[0] && (e = hipEventRecord(tev[0], s)) != hipSuccess) ||
+            (e = hipEventRecord(p->fork, s)) != hipSuccess ||
+            (e = hipStreamWaitEvent(p->side, p->fork, 0)) != hipSuccess)
+            return fail(UA_ERR_HIP, "fork: %s", hipGetErrorString(e));
     }
-    if (e != hipSuccess) return fail(UA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    // the wide launch first (it holds the longest workgroups), then stream-K
+    for (int i = pl.n - 1; i >= 0; --i) {
+        const Sub& g = pl.sub[i];
+        UaKernelParams kp = base;
+        kp.block_q = g.block_q;
+        kp.rows_used = g.block_q * p->group;
+        kp.tile_n = g.tile_n;
+        kp.tiles_per_seg = g.tiles_per_seg;
+        kp.num_segments = g.num_segments;
+        kp.class_mode = g.class_mode;
+        UaLaunch l{};
+        l.path = g.path;
+        l.waves = g.waves;
+        l.tile_n = g.tile_n;
+        l.head_dim = d.head_dim;
+        l.q_dtype = d.q_dtype;
+        l.kv_fp8 = p->fp8;
+        l.stream_k = g.stream_k;
+        for (int j = 0; j < 3; ++j) l.grid[j] = g.grid[j];
+        l.reduce_rows = a->total_q * d.num_q_heads;
+        if (g.path == 3 && g.stream_k) {
+            float* ws = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + seg_bytes);
+            const size_t rows =
+                ((size_t)a->num_seqs * d.num_kv_heads + kMaxStreamKWorkers) * kp.rows_used;
+            kp.ws_o = ws;
+            kp.ws_m = ws + rows * d.head_dim;
+            kp.ws_l = kp.ws_m + rows;
+            // enumerate reduce rows by (sequence, head, position) when most
+            // tokens belong to the other launch
+            const int64_t by_seq = (int64_t)a->num_seqs * d.num_q_heads * kp.small_block_q;
+            kp.reduce_by_seq = g.class_mode == 1 && by_seq < l.reduce_rows;
+            if (kp.reduce_by_seq) l.reduce_rows = by_seq;
+        } else if (g.path == 3) {
+            const size_t rows = (size_t)a->total_q * d.num_q_heads;
+            float* ws = static_cast<float*>(a->workspace);
+            kp.ws_o = ws;
+            kp.ws_m = ws + rows * g.num_segments * d.head_dim;
+            kp.ws_l = kp.ws_m + rows * g.num_segments;
+        }
+        // timing events of a single launch: [0] before the kernel, [1] after
+        // it, [2] after its reduce; a split batch records its own around both
+        if (pl.n == 1)
+            for (int j = 0; j < 3; ++j) l.events[j] = tev[j];
+        hipStream_t st = i == 0 && pl.n == 2 ? p->side : s;
+        hipError_t e;
+        switch (d.head_dim) {
+            case 64: e = ua_launch_d64(kp, l, st); break;
+            case 128: e = ua_launch_d128(kp, l, st); break;
+            default: e = ua_launch_d256(kp, l, st); break;
+        }
+        if (e != hipSuccess) return fail(UA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
+    if (pl.n == 2) {
+        hipError_t e;
+        if ((e = hipEventRecord(p->join, p->side)) != hipSuccess ||
+            (e = hipStreamWaitEvent(s, p->join, 0)) != hipSuccess ||
+            (tev[1] && (e = hipEventRecord(tev[1], s)) != hipSuccess) ||
+            (tev[2] && (e = hipEventRecord(tev[2], s)) != hipSuccess))
+            return fail(UA_ERR_HIP, "join: %s", hipGetErrorString(e));
+    }
     return UA_OK;
 }
 

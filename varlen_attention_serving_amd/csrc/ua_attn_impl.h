@@ -75,6 +75,11 @@ constexpr int kVPad = 32;  // V LDS row padding (elements)
 constexpr int kMinWavesPerSimd = UA_MIN_WAVES_PER_SIMD;
 // four-wave workgroups with d <= 128: three resident per CU (168 VGPRs per lane)
 constexpr int kMinWavesPerSimdWide = 3;
+// d = 256 holds a 32-row O accumulator of 128 registers: one wave per SIMD for
+// the single-wave geometry, two for the four-wave one
+constexpr int min_waves_per_simd(int d, int waves) {
+    return d > 128 ? (waves >= 4 ? 2 : 1) : (waves >= 4 ? kMinWavesPerSimdWide : kMinWavesPerSimd);
+}
 // log2-unit slack before the running reference max is moved (p <= 2^8)
 constexpr float kLazyRescale = 8.0f;
 
@@ -164,6 +169,14 @@ __device__ __forceinline__ KeyRange key_range(uint32_t flags, int window, int s_
     r.full_hi = causal ? min(s_k - 1, ctx + p0) : s_k - 1;
     r.full_lo = win ? max(0, ctx + p_last - window + 1) : 0;
     return r;
+}
+
+// Split-KV pieces of a q-block with n live tiles: min(segments, ceil(n /
+// tiles)) runs of near-equal length, so runs hold at most `tiles` tiles while
+// the grid has segments to spare and ceil(n / segments) when it has not.
+// Piece i covers tiles [i n / pieces, (i + 1) n / pieces) of the range.
+__device__ __forceinline__ int seg_pieces(int n, int segments, int tiles) {
+    return n > 0 ? min(segments, (n + tiles - 1) / tiles) : 0;
 }
 
 
@@ -345,7 +358,11 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
     float mt = -INFINITY;
     auto transform = [&](float x, int key) {
         if (XFORM) {
-            x = softcap ? p.softcap_out * tanh_f32(x * p.softcap_in) : x * p.qk_scale_log2;
+            // c tanh(y) = c - 2c / (1 + e^{2y}), with e^{2y} = 2^{x * softcap_in2}: saturates
+            // to +-c for large |y| (1 / inf = 0) without a clamp
+            x = softcap ? p.softcap_out - 2.0f * p.softcap_out *
+                                              __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
+                        : x * p.qk_scale_log2;
             x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
         }
         return x;
@@ -447,7 +464,7 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // ---------------------------------------------------------------------------
 
 template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, bool XFORM>
-__global__ __launch_bounds__(NW * 64, (NW >= 4 && D <= 128) ? kMinWavesPerSimdWide : kMinWavesPerSimd) void ua_attn_kernel(UaKernelParams p) {
+__global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, NW, BN, FP8> G;
@@ -473,6 +490,7 @@ __global__ __launch_bounds__(NW * 64, (NW >= 4 && D <= 128) ? kMinWavesPerSimdWi
     const int q_len = p.cu_q[s + 1] - q_start;
     const int p0 = (slot - (q_start / p.block_q + s)) * p.block_q;
     if (p0 >= q_len) return;
+    if (p.class_mode == 2 && q_len <= p.small_block_q) return;  // the decode kernel's rows
     // S_k beyond the block table's width would read past the table (a violated
     // precondition); clamp so the gather stays inside it.
     const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
@@ -482,10 +500,13 @@ __global__ __launch_bounds__(NW * 64, (NW >= 4 && D <= 128) ? kMinWavesPerSimdWi
     int t_lo = kr.lo / BN;
     int t_hi = (kr.hi + BN - 1) / BN;
     if (SPLIT) {
-        const int a = t_lo + seg * p.tiles_per_seg;
-        if (a >= t_hi) return;
-        t_lo = a;
-        t_hi = min(t_hi, a + p.tiles_per_seg);
+        // this segment's run of the q-block's tiles; the reduce derives the
+        // same piece count
+        const int n = t_hi - t_lo;
+        const int pieces = seg_pieces(n, p.num_segments, p.tiles_per_seg);
+        if (seg >= pieces) return;
+        t_hi = t_lo + (int)((int64_t)(seg + 1) * n / pieces);
+        t_lo = t_lo + (int)((int64_t)seg * n / pieces);
     }
 
     const RowInfo ri = row_info(p, wave * 32 + (lane & 31), hk, q_start, q_len, s_k, p0);
@@ -585,6 +606,7 @@ __device__ __forceinline__ SeqLane seq_lane(const UaKernelParams& p, int s) {
     r.q_len = p.cu_q[s + 1] - r.q_start;
     r.s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
     if (r.q_len <= 0) return r;
+    if (p.class_mode == 1 && r.q_len > p.small_block_q) return r;  // another kernel's rows
     const KeyRange kr = key_range(p.flags, p.window, r.s_k, r.s_k - r.q_len, 0, r.q_len - 1);
     r.t_lo = kr.lo / BN;
     r.n = max(0, (kr.hi + BN - 1) / BN - r.t_lo);
@@ -696,7 +718,7 @@ __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int
 }
 
 template <int D, int BN, typename QT, bool FP8, bool XFORM>
-__global__ __launch_bounds__(64, kMinWavesPerSimd) void ua_decode_sk_kernel(UaKernelParams p) {
+__global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, 1, BN, FP8> G;
@@ -854,10 +876,32 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
     const int tok = (int)(row / p.num_q_heads);
     const int head = (int)(row - (int64_t)tok * p.num_q_heads);
 
-    if (SK) {
+    if (SK && p.reduce_by_seq) {
+        // rows enumerated as (sequence, query head, local position)
+        const int per_seq = p.num_q_heads * p.small_block_q;
+        const int s = (int)(row / per_seq);
+        const int rem = (int)(row - (int64_t)s * per_seq);
+        const int head2 = rem / p.small_block_q;
+        const int i = rem - head2 * p.small_block_q;
+        const int q_start = p.cu_q[s];
+        const int q_len = p.cu_q[s + 1] - q_start;
+        if (i >= q_len || q_len > p.small_block_q) return;
+        int n, total;
+        const int xs = sk_seq_prefix<kSkTile>(p, s, &n, &total);
+        const int64_t T = total;
+        const int64_t W = p.sk_workers;
+        const int hk = head2 / p.group;
+        const int64_t x0 = xs + (int64_t)hk * n;
+        const int j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
+        const int j1 = T > 0 ? sk_worker_of(x0 + n - 1, T, W) : 0;
+        const int r = i * p.group + (head2 - hk * p.group);
+        const int count = (n > 0 && T > 0) ? j1 - j0 + 1 : 0;
+        merge_partials<D, QT>(p, ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r,
+                              p.rows_used, count, j0, T, W, true, q_start + i, head2);
+    } else if (SK) {
         // one pass over the sequences: the token's sequence s, the first
         // flattened tile of s, its tile count and the total T
-        int carry = 0, s = -1, xs = 0, n = 0, q_start = 0;
+        int carry = 0, s = -1, xs = 0, n = 0, q_start = 0, q_len = 0;
         for (int base = 0; base < p.num_seqs; base += 64) {
             const SeqLane q = seq_lane<kSkTile>(p, base + lane);
             const int v = q.n * p.num_kv_heads;
@@ -870,9 +914,12 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
                 xs = carry + readlane(incl - v, l);
                 n = readlane(q.n, l);
                 q_start = readlane(q.q_start, l);
+                q_len = readlane(q.q_len, l);
             }
             carry += readlane(incl, 63);
         }
+        // rows of the wide launch's sequences are that launch's to write
+        if (p.class_mode == 1 && q_len > p.small_block_q) return;
         const int64_t T = carry;
         const int64_t W = p.sk_workers;
         const int hk = head / p.group;
@@ -887,6 +934,7 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const int s = token_seq(p.cu_q, p.num_seqs, tok);
         const int q_start = p.cu_q[s];
         const int q_len = p.cu_q[s + 1] - q_start;
+        if (p.class_mode == 2 && q_len <= p.small_block_q) return;  // the decode kernel's rows
         const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
         const int ctx = s_k - q_len;
         const int p0 = ((tok - q_start) / p.block_q) * p.block_q;
@@ -894,9 +942,7 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const KeyRange kr = key_range(p.flags, p.window, s_k, ctx, p0, p_last);
         const int t_lo = kr.lo / p.tile_n;
         const int t_hi = (kr.hi + p.tile_n - 1) / p.tile_n;
-        const int count = t_hi > t_lo ? min(p.num_segments, (t_hi - t_lo + p.tiles_per_seg - 1) /
-                                                                p.tiles_per_seg)
-                                      : 0;
+        const int count = seg_pieces(t_hi - t_lo, p.num_segments, p.tiles_per_seg);
         merge_partials<D, QT>(p, row * p.num_segments, 1, count, 0, 1, 1, false, tok, head);
     }
 }
@@ -981,10 +1027,6 @@ hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream
     if (l.waves == 4 && l.tile_n == 32) return launch_if_built<D, 4, 32, QT, FP8, XFORM>(p, l, st);
     if constexpr (D <= 128) {
         if (l.waves == 4 && l.tile_n == 64) return launch_if_built<D, 4, 64, QT, FP8, XFORM>(p, l, st);
-#if defined(UA_EXPERIMENT_WIDE)
-        if (l.waves == 8 && l.tile_n == 32) return launch_if_built<D, 8, 32, QT, FP8, XFORM>(p, l, st);
-        if (l.waves == 8 && l.tile_n == 64) return launch_if_built<D, 8, 64, QT, FP8, XFORM>(p, l, st);
-#endif
     }
     return hipErrorInvalidValue;
 }

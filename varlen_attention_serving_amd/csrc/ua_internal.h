@@ -36,9 +36,14 @@ struct UaKernelParams {
     int32_t window;
     float qk_scale_log2;      // tau * k_scale * log2(e)
     float softcap_in;         // tau * k_scale / c
+    float softcap_in2;        // 2 log2(e) tau * k_scale / c (argument of 2^x for e^{2y})
     float softcap_out;        // c * log2(e)
     float out_scale;          // v_scale for fp8 V, else 1
     int32_t sk_workers;       // stream-K split: number of workers W
+    int32_t class_mode;       // 0: every sequence; 1: only sequences with q_len <=
+                              // small_block_q; 2: only the others
+    int32_t small_block_q;    // query positions of a single-wave q-block (32 / g)
+    int32_t reduce_by_seq;    // stream-K reduce rows enumerated as (seq, head, i)
 };
 
 // Upper bound on stream-K workers (sizes the workspace before the device is known).
