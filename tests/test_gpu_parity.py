@@ -143,6 +143,16 @@ def test_mixed_decode_and_chunks(i):
     assert plan.class_split == 1
 
 
+@pytest.mark.parametrize("d,b", [(64, 1), (64, 4), (128, 2), (128, 4), (64, 8)])
+def test_small_block_sizes(d, b):
+    """Blocks smaller than the key rows one wave-wide LDS copy fills keep the
+    register-staged gather; the rest take the LDS ring."""
+    w = W.random_small(500 + d + b, num_seqs=4, max_q=60, max_k=200, num_q_heads=8,
+                       num_kv_heads=2, head_dim=d, block_size=b, use_sinks=True)
+    for force in ("2d", "3d"):
+        _full_check(w, force, f"b={b}/d={d}/{force}")
+
+
 @pytest.mark.parametrize("force", ["auto", "2d", "3d"])
 def test_prefill_ragged(force):
     """Self-attention prefill with lengths that are not tile multiples."""

@@ -80,6 +80,11 @@ constexpr int kMinWavesPerSimdWide = 3;
 constexpr int min_waves_per_simd(int d, int waves) {
     return d > 128 ? (waves >= 4 ? 2 : 1) : (waves >= 4 ? kMinWavesPerSimdWide : kMinWavesPerSimd);
 }
+// 16-bit K/V tiles of four-wave workgroups are copied straight into an LDS
+// ring (0 keeps every tile on the register-staged path)
+#ifndef UA_LDS_RING
+#define UA_LDS_RING 1
+#endif
 // log2-unit slack before the running reference max is moved (p <= 2^8)
 constexpr float kLazyRescale = 8.0f;
 
@@ -271,6 +276,150 @@ struct KvLoader {
 };
 
 // ---------------------------------------------------------------------------
+// K/V tiles copied global -> LDS directly (16-bit K/V, four-wave workgroups)
+// ---------------------------------------------------------------------------
+//
+// gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes to LDS at
+// M0 + 16 lane without passing through registers, so tiles can be in flight
+// while earlier ones are computed: a ring of STAGES tile buffers, with tile
+// t + STAGES - 1 issued while tile t is computed.  One copy fills 1 KB of
+// LDS, so the tile image is unpadded (rows of 2D bytes) and bank conflicts
+// are avoided by permuting the 16-byte chunks of a row instead: chunk c of
+// key row r sits in slot c ^ swz(r), and the lane that fills a slot fetches
+// the chunk that belongs there.  The copies are issued from inline assembly
+// so that the compiler, which would wait for every outstanding copy before
+// any LDS read, leaves the waiting to the explicit counter waits: before
+// computing a tile the loop waits until that tile's copies have landed
+// (later tiles' copies may stay in flight), then meets the barrier.
+
+// Per-lane LDS offsets (elements) of the K fragment read and of the
+// transposing V read; kx / vx are the lane's chunk swizzles (swizzled tiles).
+struct Frag {
+    int k, v, kx, vx;
+};
+
+template <int D>
+struct LdsGeom {
+    static constexpr int BN = 32;                   // keys per tile
+    static constexpr int RB = 2 * D;                // bytes per key row
+    static constexpr int CPR = RB / 16;             // 16-byte chunks per row
+    static constexpr int ROWS_PER_OP = 1024 / RB;   // key rows one wave-wide copy fills
+    static constexpr int OPS = 2 * BN * RB / 1024;  // copies per tile (K image, then V)
+    static constexpr int GROUPS = OPS / 8;          // row groups per wave (a K and a V copy each)
+    static constexpr int OPS_W = 2 * GROUPS;        // copies per wave per tile
+    static constexpr int STAGES = 3;
+    static constexpr int TILE_ELEMS = BN * D;       // one K or V image (16-bit elements)
+    static constexpr uint32_t STAGE_BYTES = 4 * TILE_ELEMS;
+    static_assert(OPS % 8 == 0, "four waves copy whole row groups");
+};
+
+// Chunk permutations: the K fragment read of one chunk from 16 consecutive
+// rows, and the transposing V read of 64 contiguous bytes from 4 consecutive
+// rows, each touch distinct banks.
+template <int D>
+__host__ __device__ constexpr int swz_k(int r) {
+    return D == 64 ? (r >> 1) & 7 : r & 15;
+}
+template <int D>
+__host__ __device__ constexpr int swz_v(int r) {
+    return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+}
+
+// The padded-tile lane offsets of padded_frag, moved to the swizzled image:
+// k / v are the row bases plus the swizzle-independent part of the column.
+template <int D>
+__host__ __device__ inline Frag swizzled_frag(int lane) {
+    const int g16 = lane >> 4;
+    const int m = lane & 31;
+    const int half = lane >> 5;
+    const int fk = swz_k<D>(m);
+    const int rv = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    Frag f;
+    f.k = m * D + 8 * ((half ^ fk) & 1);
+    f.kx = fk & ~1;
+    f.v = rv * D + 8 * (2 * (g16 & 1) + ((lane & 3) >> 1)) + 4 * (lane & 1);
+    f.vx = swz_v<D>(rv) >> 2;
+    return f;
+}
+
+// Where a lane's copies of one tile come from: in row group g of wave w the
+// K copy fills image bytes [1024 (w + 4 g), +1024) and the V copy the same
+// range of the V image, i.e. key rows (w + 4 g) ROWS_PER_OP + lane / CPR.
+template <int D>
+struct LdsCopy {
+    typedef LdsGeom<D> L;
+    int row[L::GROUPS];
+    int koff[L::GROUPS], voff[L::GROUPS];  // byte offsets of the fetched chunks
+
+    __host__ __device__ void init(int wave, int lane) {
+        const int cs = lane % L::CPR;
+        for (int g = 0; g < L::GROUPS; ++g) {
+            row[g] = (wave + 4 * g) * L::ROWS_PER_OP + lane / L::CPR;
+            koff[g] = 16 * (cs ^ swz_k<D>(row[g]));
+            voff[g] = 16 * (cs ^ swz_v<D>(row[g]));
+        }
+    }
+};
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// one wave-wide 16-byte-per-lane copy global -> LDS at m0 + 16 lane
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// wait until at most N of this wave's copies are outstanding and its LDS
+// reads are done, then meet the other waves
+template <int N>
+__device__ __forceinline__ void lds_tile_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt = 0 only
+constexpr int kWaitVmcntZero = 0x0F70;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+// Block ids of a tile's row groups for wave w: rows of one group lie in one
+// block (block size >= ROWS_PER_OP), so each is one scalar load.  Keys past
+// S_k are fetched from slot S_k - 1, which lies in the same group's block.
+template <int D>
+__device__ __forceinline__ void lds_tile_ids(const_i32_ptr bt_row, int t, int s_k, int lb, int wave,
+                                             int (&id)[LdsGeom<D>::GROUPS]) {
+    typedef LdsGeom<D> L;
+#pragma unroll
+    for (int g = 0; g < L::GROUPS; ++g) {
+        const int key = min(t * L::BN + (wave + 4 * g) * L::ROWS_PER_OP, s_k - 1);
+        id[g] = bt_row[__builtin_amdgcn_readfirstlane(key >> lb)];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void lds_tile_issue(const LdsCopy<D>& cp, const unsigned char* base_k,
+                                               const unsigned char* base_v, int t, int s_k, int lb,
+                                               uint64_t slot_bytes,
+                                               const int (&id)[LdsGeom<D>::GROUPS],
+                                               uint32_t m0_stage, int wave) {
+    typedef LdsGeom<D> L;
+    const int bmask = (1 << lb) - 1;
+#pragma unroll
+    for (int g = 0; g < L::GROUPS; ++g) {
+        const int key = min(t * L::BN + cp.row[g], s_k - 1);
+        const uint64_t slot = ((uint64_t)(uint32_t)id[g] << lb) + (uint32_t)(key & bmask);
+        const uint64_t off = slot * slot_bytes;
+        const uint32_t m0 = m0_stage + (uint32_t)(wave + 4 * g) * 1024u;
+        lds_copy16(base_k + off + cp.koff[g], m0);
+        lds_copy16(base_v + off + cp.voff[g], m0 + (uint32_t)(2 * L::TILE_ELEMS));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // One wave's 32 query rows against one KV tile in LDS
 // ---------------------------------------------------------------------------
 
@@ -323,14 +472,14 @@ __device__ __forceinline__ void load_q(const UaKernelParams& p, const RowInfo& r
 // scale -> softcap -> ALiBi -> masks (log2 units), the online-softmax update,
 // then O^T += V^T P^T.  key0 is the tile's first key position.  XFORM = false
 // compiles the plain scale for problems without softcap and ALiBi.
-template <int D, int BN, typename QT, bool XFORM>
+template <int D, int BN, typename QT, bool XFORM, bool SWZ = false>
 __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
                                             const unsigned short* __restrict__ k_lds,
                                             const unsigned short* __restrict__ v_lds,
                                             const typename QType<QT>::v8 (&qf)[D / 16],
                                             f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
                                             int key0, bool need_mask, const RowCtx& rc,
-                                            int k_frag, int v_frag, int half) {
+                                            const Frag& fr, int half) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     constexpr int KSTR = D + kKPad;
@@ -344,7 +493,9 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         sacc[kt] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
-            v8 a = *reinterpret_cast<const v8*>(&k_lds[k_frag + kt * 32 * KSTR + 16 * kc]);
+            const int off = SWZ ? fr.k + kt * 32 * D + 8 * ((2 * kc) ^ fr.kx)
+                                : fr.k + kt * 32 * KSTR + 16 * kc;
+            v8 a = *reinterpret_cast<const v8*>(&k_lds[off]);
             sacc[kt] = Q::mma(a, qf[kc], sacc[kt]);
         }
     }
@@ -418,9 +569,11 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const int off = v_frag + kc * 16 * VSTR + dt * 32;
+            const int off = SWZ ? fr.v + kc * 16 * D + 32 * (dt ^ fr.vx)
+                                : fr.v + kc * 16 * VSTR + dt * 32;
+            constexpr int HI = 8 * (SWZ ? D : VSTR);
             i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off]);
-            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + 8 * VSTR]);
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + HI]);
             u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
             oacc[dt] = Q::mma(__builtin_bit_cast(v8, w), pf, oacc[dt]);
@@ -428,15 +581,18 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
     }
 }
 
-// per-lane LDS offsets of the K fragment read and of the transposing V read
+// Lane offsets into padded tiles: the K fragment read takes row lane % 32,
+// elements 8 (lane / 32) + 16 kc; the transposing V read takes, per 16-lane
+// group g, key row 4 (g / 2) + (lane % 16) / 4 and elements
+// 16 (g % 2) + 4 (lane % 4) of each 32-wide d tile.
 template <int D>
-__device__ __forceinline__ int k_frag_offset(int lane) {
-    return (lane & 31) * (D + kKPad) + 8 * (lane >> 5);
-}
-template <int D>
-__device__ __forceinline__ int v_frag_offset(int lane) {
+__device__ __forceinline__ Frag padded_frag(int lane) {
     const int g16 = lane >> 4;
-    return (4 * (g16 >> 1) + ((lane & 15) >> 2)) * (D + kVPad) + 16 * (g16 & 1) + 4 * (lane & 3);
+    Frag f;
+    f.k = (lane & 31) * (D + kKPad) + 8 * (lane >> 5);
+    f.v = (4 * (g16 >> 1) + ((lane & 15) >> 2)) * (D + kVPad) + 16 * (g16 & 1) + 4 * (lane & 3);
+    f.kx = f.vx = 0;
+    return f;
 }
 
 // Un-normalised partial of the lane's row: o (fp32), the running max m (log2
@@ -463,6 +619,68 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // 2D query-tile kernel and the segmented 3D split-KV kernel
 // ---------------------------------------------------------------------------
 
+// The q-block (and, split, the run of its KV tiles) a workgroup owns; false
+// when it owns nothing.
+struct QBlockWork {
+    int s, q_start, q_len, p0, s_k, t_lo, t_hi;
+    KeyRange kr;
+};
+
+template <int BN, bool SPLIT>
+__device__ __forceinline__ bool qblock_work(const UaKernelParams& p, int slot, int seg,
+                                            QBlockWork& w) {
+    w.s = qblock_seq(p.cu_q, p.num_seqs, p.block_q, slot);
+    w.q_start = p.cu_q[w.s];
+    w.q_len = p.cu_q[w.s + 1] - w.q_start;
+    w.p0 = (slot - (w.q_start / p.block_q + w.s)) * p.block_q;
+    if (w.p0 >= w.q_len) return false;
+    if (p.class_mode == 2 && w.q_len <= p.small_block_q) return false;  // the decode kernel's rows
+    // S_k beyond the block table's width would read past the table (a violated
+    // precondition); clamp so the gather stays inside it.
+    w.s_k = min(p.seq_lens[w.s], p.bt_stride << p.block_size_log2);
+    const int p_last = min(w.p0 + p.block_q, w.q_len) - 1;
+    w.kr = key_range(p.flags, p.window, w.s_k, w.s_k - w.q_len, w.p0, p_last);
+    w.t_lo = w.kr.lo / BN;
+    w.t_hi = (w.kr.hi + BN - 1) / BN;
+    if (SPLIT) {
+        // this segment's run of the q-block's tiles; the reduce derives the
+        // same piece count
+        const int n = w.t_hi - w.t_lo;
+        const int pieces = seg_pieces(n, p.num_segments, p.tiles_per_seg);
+        if (seg >= pieces) return false;
+        w.t_hi = w.t_lo + (int)((int64_t)(seg + 1) * n / pieces);
+        w.t_lo = w.t_lo + (int)((int64_t)seg * n / pieces);
+    }
+    return true;
+}
+
+// A wave's rows after the last tile: normalised O, or the split partial.
+template <int D, typename QT, bool SPLIT>
+__device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowInfo& ri, int half,
+                                            int seg, const f32x16 (&oacc)[D / 32], float m_run,
+                                            float l_run) {
+    typedef QType<QT> Q;
+    const float l_tot = l_run + xor32(l_run);
+    if (!ri.ok) return;
+    if (SPLIT) {
+        const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
+        write_partial<D>(p, rid, half, oacc, m_run, l_tot);
+    } else {
+        const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+        QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)ri.tok * p.o_stride_tok +
+                 (int64_t)ri.head * D + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                typename Q::v4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = (QT)(oacc[dt][4 * ig + j] * inv);
+                *reinterpret_cast<typename Q::v4*>(op + 32 * dt + 8 * ig) = v;
+            }
+    }
+}
+
 template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, bool XFORM>
 __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
@@ -484,34 +702,15 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
         hk = blockIdx.x; slot = blockIdx.y; seg = 0;
     }
 
-    // ---- which sequence and positions this workgroup owns ----
-    const int s = qblock_seq(p.cu_q, p.num_seqs, p.block_q, slot);
-    const int q_start = p.cu_q[s];
-    const int q_len = p.cu_q[s + 1] - q_start;
-    const int p0 = (slot - (q_start / p.block_q + s)) * p.block_q;
-    if (p0 >= q_len) return;
-    if (p.class_mode == 2 && q_len <= p.small_block_q) return;  // the decode kernel's rows
-    // S_k beyond the block table's width would read past the table (a violated
-    // precondition); clamp so the gather stays inside it.
-    const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
-    const int ctx = s_k - q_len;
-    const int p_last = min(p0 + p.block_q, q_len) - 1;
-    const KeyRange kr = key_range(p.flags, p.window, s_k, ctx, p0, p_last);
-    int t_lo = kr.lo / BN;
-    int t_hi = (kr.hi + BN - 1) / BN;
-    if (SPLIT) {
-        // this segment's run of the q-block's tiles; the reduce derives the
-        // same piece count
-        const int n = t_hi - t_lo;
-        const int pieces = seg_pieces(n, p.num_segments, p.tiles_per_seg);
-        if (seg >= pieces) return;
-        t_hi = t_lo + (int)((int64_t)(seg + 1) * n / pieces);
-        t_lo = t_lo + (int)((int64_t)seg * n / pieces);
-    }
+    QBlockWork qb;
+    if (!qblock_work<BN, SPLIT>(p, slot, seg, qb)) return;
+    const int s = qb.s, s_k = qb.s_k;
+    const KeyRange kr = qb.kr;
+    const int t_lo = qb.t_lo, t_hi = qb.t_hi;
 
-    const RowInfo ri = row_info(p, wave * 32 + (lane & 31), hk, q_start, q_len, s_k, p0);
+    const RowInfo ri = row_info(p, wave * 32 + (lane & 31), hk, qb.q_start, qb.q_len, s_k, qb.p0);
     const int r0 = wave * 32;
-    const bool wave_active = r0 < p.rows_used && p0 + r0 / p.group < q_len;
+    const bool wave_active = r0 < p.rows_used && qb.p0 + r0 / p.group < qb.q_len;
     v8 qf[D / 16];
     load_q<D, QT>(p, ri, half, qf);
 
@@ -536,8 +735,7 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
         reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * G::ESZ;
     KvLoader<D, NW, BN, QT, FP8> ld;
     ld.init(tid);
-    const int k_frag = k_frag_offset<D>(lane);
-    const int v_frag = v_frag_offset<D>(lane);
+    const Frag fr = padded_frag<D>(lane);
 
     ld.ids(bt, t_lo, s_k, lb);
     ld.load(base_k, base_v, t_lo, s_k, lb, slot_bytes);
@@ -554,29 +752,113 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
         const int key0 = t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
         attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
-                               k_frag, v_frag, half);
+                               fr, half);
     }
 
     if (!wave_active) return;
-    const float l_tot = l_run + xor32(l_run);
-    if (!ri.ok) return;
+    finish_rows<D, QT, SPLIT>(p, ri, half, seg, oacc, m_run, l_run);
+}
+
+// The same q-block work for 16-bit K/V with four waves and block sizes of at
+// least ROWS_PER_OP keys: tiles arrive through the LDS ring instead of
+// registers (STAGES - 1 tiles in flight, one barrier per tile).
+template <int D, typename QT, bool SPLIT, bool XFORM>
+__global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_kernel(UaKernelParams p) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    typedef LdsGeom<D> L;
+    constexpr int BN = L::BN;
+    constexpr int S = L::STAGES;
+
+    __shared__ __attribute__((aligned(1024))) unsigned short tiles[S * 2 * L::TILE_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+
+    int hk, slot, seg;
     if (SPLIT) {
-        const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
-        write_partial<D>(p, rid, half, oacc, m_run, l_tot);
+        slot = blockIdx.x; hk = blockIdx.y; seg = blockIdx.z;
     } else {
-        const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
-        QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)ri.tok * p.o_stride_tok +
-                 (int64_t)ri.head * D + 4 * half;
-#pragma unroll
-        for (int dt = 0; dt < G::NDT; ++dt)
-#pragma unroll
-            for (int ig = 0; ig < 4; ++ig) {
-                typename Q::v4 v;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = (QT)(oacc[dt][4 * ig + j] * inv);
-                *reinterpret_cast<typename Q::v4*>(op + 32 * dt + 8 * ig) = v;
-            }
+        hk = blockIdx.x; slot = blockIdx.y; seg = 0;
     }
+
+    QBlockWork qb;
+    if (!qblock_work<BN, SPLIT>(p, slot, seg, qb)) return;
+    const int s_k = qb.s_k;
+    const KeyRange kr = qb.kr;
+    const int t_lo = qb.t_lo, t_hi = qb.t_hi;
+
+    const RowInfo ri = row_info(p, wave * 32 + (lane & 31), hk, qb.q_start, qb.q_len, s_k, qb.p0);
+    const bool wave_active = wave * 32 < p.rows_used && qb.p0 + wave * 32 / p.group < qb.q_len;
+    v8 qf[D / 16];
+    load_q<D, QT>(p, ri, half, qf);
+
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+    if (!SPLIT && (p.flags & UA_FLAG_SINKS)) {
+        m_run = p.sinks[ri.head] * kLog2e;
+        l_run = half == 0 ? 1.0f : 0.0f;
+    }
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+
+    const int lb = p.block_size_log2;
+    const const_i32_ptr bt = (const_i32_ptr)(p.block_table + (int64_t)qb.s * p.bt_stride);
+    const uint64_t slot_bytes = (uint64_t)p.kv_slot_stride * 2;
+    const unsigned char* base_k = reinterpret_cast<const unsigned char*>(p.k) + (int64_t)hk * D * 2;
+    const unsigned char* base_v = reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * 2;
+    LdsCopy<D> cp;
+    cp.init(wave, lane);
+    const Frag fr = swizzled_frag<D>(lane);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(tiles));
+
+    // The compiler cannot see the copies, so let it retire its own loads (Q,
+    // row facts) here: a wait it placed inside the loop would also wait for
+    // the copies in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntZero);
+    // prologue: tiles t_lo .. t_lo + S - 2 into stages 0 .. S - 2
+    int id[L::GROUPS];
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) {
+        if (t_lo + i < t_hi) {
+            lds_tile_ids<D>(bt, t_lo + i, s_k, lb, wave, id);
+            lds_tile_issue<D>(cp, base_k, base_v, t_lo + i, s_k, lb, slot_bytes, id,
+                              lds0 + (uint32_t)i * L::STAGE_BYTES, wave);
+        }
+    }
+    // ids of the next tile to issue, fetched one iteration ahead of use
+    if (t_lo + S - 1 < t_hi) lds_tile_ids<D>(bt, t_lo + S - 1, s_k, lb, wave, id);
+
+    int st = 0;  // stage holding tile t
+    for (int t = t_lo; t < t_hi; ++t) {
+        // tile t has landed (tile t + 1 may still be in flight) and every
+        // wave is done with tile t - 1, whose stage is refilled next
+        if (S > 2 && t + 1 < t_hi)
+            lds_tile_barrier<L::OPS_W>();
+        else
+            lds_tile_barrier<0>();
+        const int t_next = t + S - 1;
+        if (t_next < t_hi) {
+            const int st_next = st == 0 ? S - 1 : st - 1;
+            lds_tile_issue<D>(cp, base_k, base_v, t_next, s_k, lb, slot_bytes, id,
+                              lds0 + (uint32_t)st_next * L::STAGE_BYTES, wave);
+            if (t_next + 1 < t_hi) lds_tile_ids<D>(bt, t_next + 1, s_k, lb, wave, id);
+        }
+        if (wave_active) {
+            const unsigned short* k_lds = tiles + st * 2 * L::TILE_ELEMS;
+            const int key0 = t * BN;
+            const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
+            attend_tile<D, BN, QT, XFORM, true>(p, k_lds, k_lds + L::TILE_ELEMS, qf, oacc, m_run,
+                                                l_run, key0, need_mask, ri.rc, fr, half);
+        }
+        st = st + 1 == S ? 0 : st + 1;
+    }
+
+    if (!wave_active) return;
+    finish_rows<D, QT, SPLIT>(p, ri, half, seg, oacc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -758,8 +1040,7 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
 
     KvLoader<D, 1, BN, QT, FP8> ld;
     ld.init(lane);
-    const int k_frag = k_frag_offset<D>(lane);
-    const int v_frag = v_frag_offset<D>(lane);
+    const Frag fr = padded_frag<D>(lane);
     ld.ids(bt_row(pc), pc.t, pc.s_k, lb);
     ld.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
     if (A + 1 < B) ld.ids(bt_row(p1), p1.t, p1.s_k, lb);
@@ -792,7 +1073,7 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
         attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
-                               k_frag, v_frag, half);
+                               fr, half);
         if (x + 1 == B || pc.t + 1 == pc.t_end) {
             const float l_tot = l_run + xor32(l_run);
             if (ri.ok) {
@@ -992,16 +1273,30 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         } else {
             return hipErrorInvalidValue;
         }
-    } else if (l.path == 3) {
-        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XFORM>), grid, dim3(NW * 64), 0, st, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
-        hipLaunchKernelGGL((ua_reduce_kernel<D, QT, false>), dim3(nb), dim3(256), 0, st, p,
-                           l.reduce_rows);
     } else {
-        hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false, XFORM>), grid, dim3(NW * 64), 0, st, p);
+        // 16-bit K/V in four-wave workgroups take the LDS ring when one
+        // wave-wide copy's key rows always share a block (d <= 128: at
+        // d = 256 the O and Q registers leave no room for the ring's)
+        constexpr bool ring_built = UA_LDS_RING && NW == 4 && BN == LdsGeom<D>::BN && !FP8 && D <= 128;
+        const bool ring = ring_built && (1 << p.block_size_log2) >= LdsGeom<D>::ROWS_PER_OP;
+        const bool split = l.path == 3;
+        if constexpr (ring_built) {
+            if (ring && split)
+                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, true, XFORM>), grid, dim3(256), 0, st, p);
+            if (ring && !split)
+                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, false, XFORM>), grid, dim3(256), 0, st, p);
+        }
+        if (!ring && split)
+            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XFORM>), grid, dim3(NW * 64),
+                               0, st, p);
+        if (!ring && !split)
+            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false, XFORM>), grid, dim3(NW * 64),
+                               0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
+        if (split)
+            hipLaunchKernelGGL((ua_reduce_kernel<D, QT, false>), dim3(nb), dim3(256), 0, st, p,
+                               l.reduce_rows);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (l.events[2] && (e = hipEventRecord(l.events[2], st)) != hipSuccess) return e;
