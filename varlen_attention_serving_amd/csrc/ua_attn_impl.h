@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ua.h"
 #include "ua_internal.h"
@@ -97,6 +98,11 @@ template <> struct QType<__bf16> {
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    // c + a + b in fp32 (one dot2 against (1, 1))
+    static __device__ __forceinline__ float sum2(__bf16 a, __bf16 b, float c) {
+        const bf16x2 x = {a, b}, one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(x, one, c, false);
+    }
     // two e4m3 codes from the low (hi=false) or high half of `w`
     static __device__ __forceinline__ u32x2 cvt_fp8x4(unsigned w) {
         bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
@@ -109,6 +115,10 @@ template <> struct QType<_Float16> {
     typedef f16x4 v4;
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float sum2(_Float16 a, _Float16 b, float c) {
+        const f16x2 x = {a, b}, one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(x, one, c, false);
     }
     static __device__ __forceinline__ u32x2 cvt_fp8x4(unsigned w) {
         f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false);
@@ -124,13 +134,6 @@ __device__ __forceinline__ float xor32(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-// tanh(y) = sign(y) (1 - e^{-2|y|}) / (1 + e^{-2|y|}), with e^z via 2^(z log2 e)
-__device__ __forceinline__ float tanh_f32(float y) {
-    float e = fast_exp2(-2.0f * kLog2e * fabsf(y));
-    float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
-    return copysignf(t, y);
 }
 
 // Number of indices j in [1, n) with pred(j); every lane of the wave gets it.
@@ -350,13 +353,18 @@ struct LdsCopy {
     typedef LdsGeom<D> L;
     int row[L::GROUPS];
     int koff[L::GROUPS], voff[L::GROUPS];  // byte offsets of the fetched chunks
+    // byte offsets from the group's first key row (that row's slot in the
+    // caches is the copy's scalar base when every key of the tile is valid)
+    uint32_t krel[L::GROUPS], vrel[L::GROUPS];
 
-    __host__ __device__ void init(int wave, int lane) {
+    __host__ __device__ void init(int wave, int lane, uint32_t slot_bytes) {
         const int cs = lane % L::CPR;
         for (int g = 0; g < L::GROUPS; ++g) {
             row[g] = (wave + 4 * g) * L::ROWS_PER_OP + lane / L::CPR;
             koff[g] = 16 * (cs ^ swz_k<D>(row[g]));
             voff[g] = 16 * (cs ^ swz_v<D>(row[g]));
+            krel[g] = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)koff[g];
+            vrel[g] = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)voff[g];
         }
     }
 };
@@ -366,6 +374,12 @@ struct LdsCopy {
 // one wave-wide 16-byte-per-lane copy global -> LDS at m0 + 16 lane
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+// the same copy from a scalar base plus a 32-bit lane offset
+__device__ __forceinline__ void lds_copy16_s(uint32_t lane_off, const void* base, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base),
+                 "s"(m0)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -400,6 +414,10 @@ __device__ __forceinline__ void lds_tile_ids(const_i32_ptr bt_row, int t, int s_
     }
 }
 
+// Issue tile t's copies into the stage at LDS byte address m0_stage.  A tile
+// whose keys are all below S_k addresses each copy as the scalar slot of its
+// group's first row plus the lane's fixed offset; the last, partial tile
+// clamps every lane's key to S_k - 1 in 64-bit lane addresses.
 template <int D>
 __device__ __forceinline__ void lds_tile_issue(const LdsCopy<D>& cp, const unsigned char* base_k,
                                                const unsigned char* base_v, int t, int s_k, int lb,
@@ -408,6 +426,18 @@ __device__ __forceinline__ void lds_tile_issue(const LdsCopy<D>& cp, const unsig
                                                uint32_t m0_stage, int wave) {
     typedef LdsGeom<D> L;
     const int bmask = (1 << lb) - 1;
+    if ((t + 1) * L::BN <= s_k) {
+#pragma unroll
+        for (int g = 0; g < L::GROUPS; ++g) {
+            const int first = t * L::BN + (wave + 4 * g) * L::ROWS_PER_OP;
+            const uint64_t slot = ((uint64_t)(uint32_t)id[g] << lb) + (uint32_t)(first & bmask);
+            const uint64_t off = slot * slot_bytes;
+            const uint32_t m0 = m0_stage + (uint32_t)(wave + 4 * g) * 1024u;
+            lds_copy16_s(cp.krel[g], base_k + off, m0);
+            lds_copy16_s(cp.vrel[g], base_v + off, m0 + (uint32_t)(2 * L::TILE_ELEMS));
+        }
+        return;
+    }
 #pragma unroll
     for (int g = 0; g < L::GROUPS; ++g) {
         const int key = min(t * L::BN + cp.row[g], s_k - 1);
@@ -562,11 +592,10 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         const int kt = kc >> 1, q8 = (kc & 1) * 8;
         v8 pf;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float e = fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
-            l_run += e;
-            pf[j] = (QT)e;
-        }
+        for (int j = 0; j < 8; ++j) pf[j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
+        // the denominator sums the same rounded p the PV product uses
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[j], pf[j + 1], l_run);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int off = SWZ ? fr.v + kc * 16 * D + 32 * (dt ^ fr.vx)
@@ -811,7 +840,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     const unsigned char* base_k = reinterpret_cast<const unsigned char*>(p.k) + (int64_t)hk * D * 2;
     const unsigned char* base_v = reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * 2;
     LdsCopy<D> cp;
-    cp.init(wave, lane);
+    cp.init(wave, lane, (uint32_t)slot_bytes);
     const Frag fr = swizzled_frag<D>(lane);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(tiles));
 
@@ -819,7 +848,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     // row facts) here: a wait it placed inside the loop would also wait for
     // the copies in flight.
     __builtin_amdgcn_s_waitcnt(kWaitVmcntZero);
-    // prologue: tiles t_lo .. t_lo + S - 2 into stages 0 .. S - 2
+    // prologue: tiles t_lo, t_lo + 1 into stages 0, 1
     int id[L::GROUPS];
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) {
@@ -832,29 +861,35 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     // ids of the next tile to issue, fetched one iteration ahead of use
     if (t_lo + S - 1 < t_hi) lds_tile_ids<D>(bt, t_lo + S - 1, s_k, lb, wave, id);
 
-    int st = 0;  // stage holding tile t
-    for (int t = t_lo; t < t_hi; ++t) {
+    // Tile t sits in stage (t - t_lo) % 3.  The loop is unrolled by the ring
+    // size so every stage address is a constant of the instructions.
+    auto step = [&](auto stage_c, int t) {
+        constexpr int ST = decltype(stage_c)::value;
         // tile t has landed (tile t + 1 may still be in flight) and every
         // wave is done with tile t - 1, whose stage is refilled next
-        if (S > 2 && t + 1 < t_hi)
+        if (t + 1 < t_hi)
             lds_tile_barrier<L::OPS_W>();
         else
             lds_tile_barrier<0>();
         const int t_next = t + S - 1;
         if (t_next < t_hi) {
-            const int st_next = st == 0 ? S - 1 : st - 1;
             lds_tile_issue<D>(cp, base_k, base_v, t_next, s_k, lb, slot_bytes, id,
-                              lds0 + (uint32_t)st_next * L::STAGE_BYTES, wave);
+                              lds0 + (uint32_t)((ST + S - 1) % S) * L::STAGE_BYTES, wave);
             if (t_next + 1 < t_hi) lds_tile_ids<D>(bt, t_next + 1, s_k, lb, wave, id);
         }
         if (wave_active) {
-            const unsigned short* k_lds = tiles + st * 2 * L::TILE_ELEMS;
+            const unsigned short* k_lds = tiles + ST * 2 * L::TILE_ELEMS;
             const int key0 = t * BN;
             const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
             attend_tile<D, BN, QT, XFORM, true>(p, k_lds, k_lds + L::TILE_ELEMS, qf, oacc, m_run,
                                                 l_run, key0, need_mask, ri.rc, fr, half);
         }
-        st = st + 1 == S ? 0 : st + 1;
+    };
+    static_assert(S == 3, "the loop is unrolled for three stages");
+    for (int t = t_lo; t < t_hi; t += 3) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < t_hi) step(std::integral_constant<int, 1>{}, t + 1);
+        if (t + 2 < t_hi) step(std::integral_constant<int, 2>{}, t + 2);
     }
 
     if (!wave_active) return;
@@ -1278,7 +1313,8 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         // wave-wide copy's key rows always share a block (d <= 128: at
         // d = 256 the O and Q registers leave no room for the ring's)
         constexpr bool ring_built = UA_LDS_RING && NW == 4 && BN == LdsGeom<D>::BN && !FP8 && D <= 128;
-        const bool ring = ring_built && (1 << p.block_size_log2) >= LdsGeom<D>::ROWS_PER_OP;
+        const bool ring = ring_built && (1 << p.block_size_log2) >= LdsGeom<D>::ROWS_PER_OP &&
+                          p.kv_slot_stride * 2 * LdsGeom<D>::ROWS_PER_OP < (int64_t(1) << 31);
         const bool split = l.path == 3;
         if constexpr (ring_built) {
             if (ring && split)
