@@ -499,27 +499,17 @@ __device__ __forceinline__ void load_q(const UaKernelParams& p, const RowInfo& r
     }
 }
 
-// scale -> softcap -> ALiBi -> masks (log2 units), the online-softmax update,
-// then O^T += V^T P^T.  key0 is the tile's first key position.  XFORM = false
-// compiles the plain scale for problems without softcap and ALiBi.
-template <int D, int BN, typename QT, bool XFORM, bool SWZ = false>
-__device__ __forceinline__ void attend_tile(const UaKernelParams& p,
-                                            const unsigned short* __restrict__ k_lds,
-                                            const unsigned short* __restrict__ v_lds,
-                                            const typename QType<QT>::v8 (&qf)[D / 16],
-                                            f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
-                                            int key0, bool need_mask, const RowCtx& rc,
-                                            const Frag& fr, int half) {
+// S^T = K Q^T for one tile: sacc[kt] holds keys 32 kt .. 32 kt + 31 of the
+// tile against the lane's query row (raw scores).
+template <int D, int BN, typename QT, bool SWZ>
+__device__ __forceinline__ void qk_tile(const unsigned short* __restrict__ k_lds,
+                                        const typename QType<QT>::v8 (&qf)[D / 16], const Frag& fr,
+                                        f32x16 (&sacc)[BN / 32]) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     constexpr int KSTR = D + kKPad;
-    constexpr int VSTR = D + kVPad;
-    constexpr int NKT = BN / 32;
-    constexpr int NDT = D / 32;
-
-    f32x16 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
+    for (int kt = 0; kt < BN / 32; ++kt) {
         sacc[kt] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
@@ -529,7 +519,16 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
             sacc[kt] = Q::mma(a, qf[kc], sacc[kt]);
         }
     }
+}
 
+// Scores of one tile to log2 units with masks applied, and the running max
+// (O and l are re-based here when the reference max moves).
+template <int D, int BN, bool XFORM>
+__device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sacc)[BN / 32],
+                                            f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                            int key0, bool need_mask, const RowCtx& rc, int half) {
+    constexpr int NKT = BN / 32;
+    constexpr int NDT = D / 32;
     // Scores to log2 units.  Without softcap/ALiBi the multiplier c > 0 keeps
     // the order, so the max is taken on raw scores and the scale is folded
     // into the exponent as one FMA: 2^(x c - m).
@@ -585,19 +584,40 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
     }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+}
 
+// p = 2^(x c - m) in the Q type, and the running denominator.
+template <int BN, typename QT, bool XFORM>
+__device__ __forceinline__ void softmax_exp(const UaKernelParams& p, const f32x16 (&sacc)[BN / 32],
+                                            float m_run, float& l_run,
+                                            typename QType<QT>::v8 (&pf)[BN / 16]) {
+    typedef QType<QT> Q;
+    const float c = XFORM ? 1.0f : p.qk_scale_log2;
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
         const int kt = kc >> 1, q8 = (kc & 1) * 8;
-        v8 pf;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
+        for (int j = 0; j < 8; ++j)
+            pf[kc][j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
         // the denominator sums the same rounded p the PV product uses
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[j], pf[j + 1], l_run);
+        for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[kc][j], pf[kc][j + 1], l_run);
+    }
+}
+
+// O^T += V^T P^T for one tile, V^T read transposed from LDS.
+template <int D, int BN, typename QT, bool SWZ>
+__device__ __forceinline__ void pv_tile(const unsigned short* __restrict__ v_lds,
+                                        const typename QType<QT>::v8 (&pf)[BN / 16],
+                                        f32x16 (&oacc)[D / 32], const Frag& fr) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    constexpr int VSTR = D + kVPad;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+    for (int kc = 0; kc < BN / 16; ++kc) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
             const int off = SWZ ? fr.v + kc * 16 * D + 32 * (dt ^ fr.vx)
                                 : fr.v + kc * 16 * VSTR + dt * 32;
             constexpr int HI = 8 * (SWZ ? D : VSTR);
@@ -605,9 +625,29 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
             i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + HI]);
             u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
-            oacc[dt] = Q::mma(__builtin_bit_cast(v8, w), pf, oacc[dt]);
+            oacc[dt] = Q::mma(__builtin_bit_cast(v8, w), pf[kc], oacc[dt]);
         }
     }
+}
+
+// One tile: scores, scale -> softcap -> ALiBi -> masks (log2 units), the
+// online-softmax update, then O^T += V^T P^T.  key0 is the tile's first key
+// position.  XFORM = false compiles the plain scale for problems without
+// softcap and ALiBi.
+template <int D, int BN, typename QT, bool XFORM, bool SWZ = false>
+__device__ __forceinline__ void attend_tile(const UaKernelParams& p,
+                                            const unsigned short* __restrict__ k_lds,
+                                            const unsigned short* __restrict__ v_lds,
+                                            const typename QType<QT>::v8 (&qf)[D / 16],
+                                            f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                            int key0, bool need_mask, const RowCtx& rc,
+                                            const Frag& fr, int half) {
+    f32x16 sacc[BN / 32];
+    typename QType<QT>::v8 pf[BN / 16];
+    qk_tile<D, BN, QT, SWZ>(k_lds, qf, fr, sacc);
+    softmax_max<D, BN, XFORM>(p, sacc, oacc, m_run, l_run, key0, need_mask, rc, half);
+    softmax_exp<BN, QT, XFORM>(p, sacc, m_run, l_run, pf);
+    pv_tile<D, BN, QT, SWZ>(v_lds, pf, oacc, fr);
 }
 
 // Lane offsets into padded tiles: the K fragment read takes row lane % 32,
@@ -661,8 +701,13 @@ __device__ __forceinline__ bool qblock_work(const UaKernelParams& p, int slot, i
     w.s = qblock_seq(p.cu_q, p.num_seqs, p.block_q, slot);
     w.q_start = p.cu_q[w.s];
     w.q_len = p.cu_q[w.s + 1] - w.q_start;
-    w.p0 = (slot - (w.q_start / p.block_q + w.s)) * p.block_q;
-    if (w.p0 >= w.q_len) return false;
+    // A sequence's q-blocks are dispatched last block first: under a causal
+    // mask the late blocks carry the most keys, so the long workgroups start
+    // early and the short ones fill the tail.
+    const int local = slot - (w.q_start / p.block_q + w.s);
+    const int blocks = (w.q_len + p.block_q - 1) / p.block_q;
+    if (local >= blocks) return false;
+    w.p0 = (blocks - 1 - local) * p.block_q;
     if (p.class_mode == 2 && w.q_len <= p.small_block_q) return false;  // the decode kernel's rows
     // S_k beyond the block table's width would read past the table (a violated
     // precondition); clamp so the gather stays inside it.
