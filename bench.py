@@ -176,6 +176,10 @@ def main():
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
                              "variant_mix", "tiny_varlen"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scratch buffer between timed steps (outside the "
+                         "events) so no step finds K/V in L2 or the MALL; value then comes "
+                         "from the summed step events instead of the wall clock")
     ap.add_argument("--segment-tiles", type=int, default=0,
                     help="split-KV segment length in KV tiles (0 = the plan's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -248,18 +252,25 @@ def main():
             e.record(stream)
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
+    print(f"[bench] timing {args.steps} steps{' (cold)' if args.cold else ''}", file=sys.stderr,
+          flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 255)
         for j in range(3):
             run_args.timing_events[j] = evs[i][j].cuda_event
         B.ua_run(handle, run_args, stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    attn_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]))
-    step_gpu_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][2]) for i in range(args.steps)]))
+    attn_each = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)])
+    step_each = np.array([evs[i][0].elapsed_time(evs[i][2]) for i in range(args.steps)])
+    attn_ms = float(np.mean(attn_each))
+    step_gpu_ms = float(np.mean(step_each))
+    # warm: whole-job wall clock over the K steps; cold: the steps' own GPU time
+    ms_per_step = step_gpu_ms if args.cold else wall * 1e3 / args.steps
 
     if bound == "hbm":
         value = work["bytes"] / (ms_per_step * 1e-3) / 1e9
@@ -313,6 +324,9 @@ def main():
             "dense_equivalent_flops": work["dense_flops"],
             "gpu_ms_per_step_events": round(step_gpu_ms, 5),
             "attention_kernel_ms": round(attn_ms, 5),
+            "attention_kernel_ms_median": round(float(np.median(attn_each)), 5),
+            "attention_kernel_ms_min": round(float(np.min(attn_each)), 5),
+            "cache": "cold (512 MiB flush between steps)" if args.cold else "warm",
             "roofline_frac_whole_step": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
         },
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,

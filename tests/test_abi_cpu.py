@@ -176,12 +176,14 @@ def _named_plan(name, extra=0, split_segment_tiles=0):
 
 
 @pytest.mark.parametrize("name,path,split", [("tiny_varlen", 2, 0), ("decode_batch", 3, 0),
-                                             ("chunked_prefill_mix", 3, 1),
-                                             ("long_prefill", 2, 1), ("variant_mix", 3, 1)])
+                                             ("chunked_prefill_mix", 2, 0),
+                                             ("long_prefill", 2, 0), ("variant_mix", 3, 1)])
 def test_shape_rule(name, path, split):
     """2D when the q-block x kv-head grid fills the device or a q-block visits
     few keys (short context or a short window); otherwise the split path.
-    Wide batches send their decode-shaped sequences to a stream-K launch."""
+    Wide batches on the register-staged path (fp8 K/V, d = 256) send their
+    decode-shaped sequences to a stream-K launch; on the LDS ring a batch
+    whose full grid fills one resident round stays one 2D launch."""
     plan, ws = _named_plan(name)
     assert plan.path == path
     assert plan.class_split == split
@@ -191,7 +193,7 @@ def test_shape_rule(name, path, split):
         assert plan.waves == 4 and plan.stream_k == 1
     if path == 2:
         assert plan.num_segments == 1 and plan.grid[2] == 1
-    if name in ("chunked_prefill_mix", "variant_mix"):
+    if name == "variant_mix":
         # the window bounds the keys a q-block visits: segments cover that span
         assert plan.num_segments >= 2 and plan.tiles_per_segment >= 4
     assert ws < (3 << 30)
@@ -209,7 +211,7 @@ def test_segment_override_selects_the_segmented_split():
 def test_forced_paths_and_geometry():
     plan, _ = _named_plan("long_prefill", B.UA_FLAG_FORCE_3D)
     assert plan.path == 3 and plan.waves == 4 and plan.block_q == 8 and plan.class_split == 0
-    plan, _ = _named_plan("chunked_prefill_mix", B.UA_FLAG_FORCE_2D)
+    plan, _ = _named_plan("variant_mix", B.UA_FLAG_FORCE_2D)
     assert plan.path == 2 and plan.class_split == 0
     plan, _ = _named_plan("decode_batch", B.UA_FLAG_FORCE_2D)
     assert plan.path == 2 and plan.waves == 1 and plan.block_m == 32

@@ -116,19 +116,25 @@ def test_stream_k_ragged_decode(seed, hk):
 
 
 MIXED = [
-    ("plain", dict(), (32, 8, 128, 16)),
-    ("window_softcap", dict(window=300, softcap=30.0), (32, 8, 128, 32)),
+    # (name, flags, shape, class split expected)
+    ("plain", dict(), (32, 8, 128, 16), 0),
+    ("window_softcap", dict(window=300, softcap=30.0), (32, 8, 128, 32), 0),
     ("fp8_alibi_sinks_window", dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True,
-                                    use_sinks=True, window=200), (16, 2, 256, 64)),
-    ("d64_g2", dict(use_sinks=True), (8, 4, 64, 16)),
+                                    use_sinks=True, window=200), (16, 2, 256, 64), 1),
+    ("d64_g2", dict(use_sinks=True), (8, 4, 64, 16), 0),
+    ("fp8_d128_softcap", dict(kv_dtype=W.DT_FP8_E4M3, softcap=20.0), (32, 8, 128, 16), 1),
+    ("bf16_d256_window", dict(window=150, use_sinks=True), (16, 4, 256, 32), 1),
+    ("fp8_d64_g4", dict(kv_dtype=W.DT_FP8_E4M3), (16, 4, 64, 16), 1),
 ]
 
 
 @pytest.mark.parametrize("i", range(len(MIXED)))
 def test_mixed_decode_and_chunks(i):
-    """Decode rows and multi-row chunks in one batch: the decode-shaped
-    sequences run in the stream-K launch, the rest in the wide launch."""
-    name, flags, (hq, hk, d, b) = MIXED[i]
+    """Decode rows and multi-row chunks in one batch.  On the register-staged
+    wide path the decode-shaped sequences run in the concurrent stream-K
+    launch and the rest in the wide launch (class split); on the LDS ring the
+    batch stays one launch."""
+    name, flags, (hq, hk, d, b), want_split = MIXED[i]
     rng = np.random.default_rng(400 + i)
     n_dec, n_chunk = 9, 3
     dec_k = rng.integers(1, 900, size=n_dec, endpoint=True)
@@ -140,7 +146,7 @@ def test_mixed_decode_and_chunks(i):
     w = W.build(f"mixed_{name}", 400 + i, q_lens[order], sk[order], num_q_heads=hq,
                 num_kv_heads=hk, head_dim=d, block_size=b, rng=rng, **flags)
     _, plan = _full_check(w, "auto")
-    assert plan.class_split == 1
+    assert plan.class_split == want_split
 
 
 @pytest.mark.parametrize("d,b", [(64, 1), (64, 4), (128, 2), (128, 4), (64, 8)])

@@ -178,11 +178,20 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         const int64_t wide_grid = (int64_t)d.num_kv_heads * (total_q / w.block_q + 1);
         two_d = wide_grid >= kWideResidentPerCU * kNumCUs;
     }
+    // Wide q-blocks of 16-bit K/V with d <= 128 run on the LDS ring, which
+    // streams a decode-shaped q-block's keys at HBM speed inside the same
+    // launch: keep the whole batch in one 2D launch once its full grid
+    // (every sequence's slots) fills a resident round.
+    const bool ring = !P.fp8 && d.head_dim <= 128;
+    if (!small && ring && (int64_t)d.num_kv_heads * w.slots >= kWideResidentPerCU * kNumCUs)
+        two_d = true;
     if (force2) two_d = true;
     if (force3) two_d = false;
 
-    // decode rows of a wide batch go to the stream-K kernel, the rest here
-    const bool split = !small && !force2 && !force3 && pl.small_block_q > 0 && sk_fits &&
+    // Otherwise (register-staged wide launches: fp8 K/V or d = 256) the
+    // decode-shaped sequences of a wide batch go to the stream-K kernel,
+    // beside the wide launch that keeps the rest.
+    const bool split = !small && !ring && !force2 && !force3 && pl.small_block_q > 0 && sk_fits &&
                        d.split_segment_tiles == 0;
     w.class_mode = split ? 2 : 0;
     size_t ws_seg = P.ws_bytes;
