@@ -7,7 +7,9 @@
 //     taken at the reader offsets, see exactly the elements the unpermuted
 //     layout would hold at those fragment positions;
 //   * reads that the LDS serves together touch distinct banks;
-//   * the scalar-base lane offsets equal the per-lane slot addresses.
+//   * the scalar-base lane offsets equal the per-lane slot addresses;
+//   * the 16-row decode engine's transposing V reads deliver V in the key
+//     order of the scores each lane holds, on distinct banks.
 // Exit status 0 when all hold; the counts of violations are printed.
 #include "ua_attn_impl.h"
 
@@ -106,10 +108,46 @@ int check_layout() {
     return bad + k_conf + v_conf;
 }
 
+// The 16-row decode engine's transposing V reads: lane L of a 16-lane group G
+// reads 4 elements at v16_frag_offset(L) (+16 d per block, +16 rows for the
+// second read); after the hardware transpose, out(16G + 4a + b)[j] =
+// in(16G + 4j + a)[b], lane l must hold V[pi(8 (l / 16) + j)][16 db + l % 16]
+// with pi(8g + j) = 4g + j (j < 4), 16 + 4g + j - 4 (j >= 4), the key order of
+// the scores the lane holds.
+template <int D>
+int check_v16() {
+    const int vstr = D + kVPad16;
+    int bad = 0, conf = 0;
+    auto elem = [&](int off, int* row, int* col) { *row = off / vstr; *col = off % vstr; };
+    for (int db = 0; db < D / 16; ++db)
+        for (int h = 0; h < 2; ++h) {
+            int in_row[64][4], in_col[64][4];
+            std::vector<int> bank(4 * 64, 0);
+            for (int L = 0; L < 64; ++L) {
+                const int off = v16_frag_offset<D>(L) + 16 * db + h * 16 * vstr;
+                if ((2 * off) % 8) ++bad;
+                for (int b = 0; b < 4; ++b) elem(off + b, &in_row[L][b], &in_col[L][b]);
+                for (int q = 0; q < 2; ++q) ++bank[(L / 16) * 64 + ((2 * off) / 4 + q) % 64];
+            }
+            for (int x : bank) conf += x > 1;
+            for (int l = 0; l < 64; ++l) {
+                const int G = l / 16, a = (l % 16) / 4, b = l % 4;
+                for (int j = 0; j < 4; ++j) {
+                    const int src = 16 * G + 4 * j + a;
+                    const int key = (h ? 16 : 0) + 4 * G + j;  // pi(8G + 4h + j)
+                    if (in_row[src][b] != key || in_col[src][b] != 16 * db + l % 16) ++bad;
+                }
+            }
+        }
+    std::printf("d=%3d (16-row V reads): violations %d, bank overlaps %d\n", D, bad, conf);
+    return bad + conf;
+}
+
 }  // namespace
 
 int main() {
-    const int bad = check_layout<64>() + check_layout<128>() + check_layout<256>();
+    const int bad = check_layout<64>() + check_layout<128>() + check_layout<256>() +
+                    check_v16<64>() + check_v16<128>() + check_v16<256>();
     std::printf(bad ? "FAIL\n" : "OK\n");
     return bad != 0;
 }

@@ -115,6 +115,31 @@ def test_stream_k_ragged_decode(seed, hk):
     assert plan.stream_k == 1
 
 
+DECODE16 = [
+    # (H_q, H_k, kv dtype, flags): d = 256 decode-shaped batches on the 16-row engine
+    (4, 4, W.DT_BF16, dict()),
+    (16, 4, W.DT_BF16, dict(use_sinks=True, window=700)),
+    (16, 2, W.DT_FP8_E4M3, dict(use_alibi=True, use_sinks=True, window=2048, q_dtype=W.DT_F16)),
+    (16, 1, W.DT_FP8_E4M3, dict(softcap=30.0)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DECODE16)))
+def test_decode16_ragged(i):
+    """d = 256 decode rows (and short chunks that still fit 16 rows) on the
+    16-row stream-K engine: lengths from 1 to many tiles, empty sequences."""
+    hq, hk, kv, flags = DECODE16[i]
+    g = hq // hk
+    rng = np.random.default_rng(600 + i)
+    n = 40
+    sk = rng.integers(1, 2500, size=n, endpoint=True)
+    ql = np.minimum(sk, rng.integers(0, max(16 // g, 1), size=n, endpoint=True))
+    w = W.build(f"decode16_{i}", 600 + i, ql, sk, num_q_heads=hq, num_kv_heads=hk, head_dim=256,
+                block_size=32, rng=rng, kv_dtype=kv, **flags)
+    _, plan = _full_check(w, "auto")
+    assert plan.stream_k == 1 and plan.block_m == 16
+
+
 MIXED = [
     # (name, flags, shape, class split expected)
     ("plain", dict(), (32, 8, 128, 16), 0),

@@ -76,6 +76,7 @@ struct Sub {
     int stream_k;      // split path: balanced workers (single-wave geometry)
     int waves, tile_n, block_m, block_q, num_segments, tiles_per_seg;
     int class_mode;    // 0 all sequences, 1 single-wave ones only, 2 the others
+    int rows16;        // stream-K with 16-row q-blocks
     int64_t slots;
     unsigned grid[3];
 };
@@ -83,7 +84,8 @@ struct Sub {
 struct Plan {
     int n;             // 1, or 2 when decode rows of a wide batch go to stream-K
     Sub sub[2];        // sub[n - 1] holds the rows of the widest geometry
-    int small_block_q; // positions of a single-wave q-block (32 / g, 0 if g > 32)
+    int small_block_q; // positions of a stream-K q-block (16 / g on the 16-row
+                       // engine, else 32 / g; 0 if g > 32)
 };
 
 // stream-K partial slots: one per (sequence, kv-head) pair plus one per worker
@@ -102,6 +104,18 @@ void geometry(const ua_problem& P, int waves, Sub* g) {
     g->tile_n = std::max(g->tile_n, waves * 64 / chunks_per_row);
     g->block_m = 32 * waves;
     g->block_q = g->block_m / P.group;
+}
+
+// Stream-K q-blocks of 16 rows (the 16x16x32 decode engine; g <= 16), taken
+// at d = 256, where the 32-row engine's accumulators hold it to one wave per
+// SIMD (measured: at d <= 128 the 32-row engine streams faster).
+bool use_rows16(const ua_problem& P) { return P.d.head_dim == 256 && P.group <= 16; }
+
+void rows16(const ua_problem& P, Sub* g) {
+    g->rows16 = 1;
+    g->tile_n = kSkTile;
+    g->block_m = 16;
+    g->block_q = 16 / P.group;
 }
 
 // The segmented split: grid z holds the segments; each q-block cuts its own
@@ -148,7 +162,7 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
                       int32_t max_k, Plan* out) {
     const ua_problem_desc_t& d = P.d;
     Plan pl{};
-    pl.small_block_q = P.group <= 32 ? 32 / P.group : 0;
+    pl.small_block_q = use_rows16(P) ? 16 / P.group : P.group <= 32 ? 32 / P.group : 0;
     const bool force2 = d.flags & UA_FLAG_FORCE_2D;
     const bool force3 = d.flags & UA_FLAG_FORCE_3D;
     // Keys one q-block can visit.  The shape rule of section 6 of the unified
@@ -199,6 +213,7 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         Sub& k = pl.sub[0];
         Sub wide = w;
         geometry(P, 1, &k);
+        if (use_rows16(P)) rows16(P, &k);
         k.slots = num_seqs;
         k.path = 3;
         k.stream_k = 1;
@@ -223,6 +238,7 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         g.grid[2] = 1;
     } else if (small && d.split_segment_tiles == 0 && sk_fits) {
         // every sequence's rows fit one q-block: balance KV tiles over workers
+        if (use_rows16(P) && (int64_t)std::max(max_q, 1) * P.group <= 16) rows16(P, &g);
         g.path = 3;
         g.stream_k = 1;
         g.grid[0] = 0;  // resident worker count, fixed at launch
@@ -490,6 +506,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         l.q_dtype = d.q_dtype;
         l.kv_fp8 = p->fp8;
         l.stream_k = g.stream_k;
+        l.rows16 = g.rows16;
         for (int j = 0; j < 3; ++j) l.grid[j] = g.grid[j];
         l.reduce_rows = a->total_q * d.num_q_heads;
         if (g.path == 3 && g.stream_k) {

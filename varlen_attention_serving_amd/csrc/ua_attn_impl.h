@@ -98,6 +98,9 @@ template <> struct QType<__bf16> {
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
     // c + a + b in fp32 (one dot2 against (1, 1))
     static __device__ __forceinline__ float sum2(__bf16 a, __bf16 b, float c) {
         const bf16x2 x = {a, b}, one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -115,6 +118,9 @@ template <> struct QType<_Float16> {
     typedef f16x4 v4;
     static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ float sum2(_Float16 a, _Float16 b, float c) {
         const f16x2 x = {a, b}, one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -1169,6 +1175,328 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
 }
 
 // ---------------------------------------------------------------------------
+// Stream-K decode with 16-row q-blocks (16x16x32 MFMA)
+// ---------------------------------------------------------------------------
+//
+// Decode rows of one (sequence, kv-head) pair are g (times the few positions
+// of a short chunk), so a 32-row tile wastes most of its accumulators.  This
+// engine packs 16 rows per wave on v_mfma_f32_16x16x32:
+//   * S^T = K Q^T per 16-key block kb: lane l holds keys 16 kb + 4 (l / 16) + i
+//     (i < 4) of query row l % 16;
+//   * K is loaded from the cache straight into the A operand (lane l: key
+//     16 kb + l % 16, elements 32 kc + 8 (l / 16) .. + 7), so K needs no LDS;
+//   * P feeds O^T += V^T P^T with the 32 keys of a tile taken in the order
+//     pi(8 g + j) = 4 g + j (j < 4), 16 + 4 g + j - 4 (j >= 4): exactly the
+//     eight scores lane l holds, so P needs no data movement;
+//   * V^T is read in that key order from a padded V tile in LDS by two
+//     transposing reads per 16 d: lane 16 G + 4 J + A reads row 4 G + J (and
+//     16 + 4 G + J), elements 16 dblk + 4 A .. + 3;
+//   * a row's max and sum combine the four lanes l % 16 + 16 {0..3}.
+// O takes 4 registers per 16 d (half the 32-row engine's), which leaves room
+// for more resident waves, i.e. more K/V bytes in flight.
+
+constexpr int kVPad16 = 16;  // V row padding (elements) of the 16-row engine
+
+template <int D, bool FP8>
+struct Geom16 {
+    static constexpr int BN = 32;
+    static constexpr int ESZ = FP8 ? 1 : 2;
+    static constexpr int VSTR = D + kVPad16;
+    static constexpr int NKC = D / 32;               // 32-element d chunks (QK steps)
+    static constexpr int NDB = D / 16;               // 16-wide d blocks (PV steps)
+    static constexpr int EPC = 16 / ESZ;             // cached elements per 16-byte chunk
+    static constexpr int CPR = D / EPC;              // chunks per key row
+    static constexpr int RSTEP = 64 / CPR;           // V rows per wave pass
+    static constexpr int NCH = BN / RSTEP;           // V chunks per lane per tile
+    static constexpr int KB = FP8 ? 8 : 16;          // bytes of one K operand load
+    static_assert(64 % CPR == 0 && BN % RSTEP == 0, "V tile rows must divide evenly");
+};
+
+template <int D, typename QT, bool FP8>
+struct Loader16 {
+    typedef Geom16<D, FP8> G;
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    // K operands of the next tile: [kb][kc], 16 bytes (8 for fp8) per lane
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type kword;
+    kword kreg[2][G::NKC];
+    u32x4 vreg[G::NCH];
+    int kphys[2], vphys[G::NCH];
+    int vcc, vrow0;
+
+    __device__ __forceinline__ void init(int lane) {
+        vcc = lane % G::CPR;
+        vrow0 = lane / G::CPR;
+    }
+    __device__ __forceinline__ void ids(const int32_t* bt_row, int t, int s_k, int lb, int lane) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = min(t * G::BN + 16 * kb + (lane & 15), s_k - 1);
+            kphys[kb] = bt_row[key >> lb];
+        }
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int key = min(t * G::BN + vrow0 + i * G::RSTEP, s_k - 1);
+            vphys[i] = bt_row[key >> lb];
+        }
+    }
+    // K straight into operand registers (keys past S_k read slot S_k - 1 and
+    // are masked); V rows as 16-byte chunks, keys past S_k zeroed
+    __device__ __forceinline__ void load(const unsigned char* base_k, const unsigned char* base_v,
+                                         int t, int s_k, int lb, int64_t slot_bytes, int lane) {
+        const int bmask = (1 << lb) - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = min(t * G::BN + 16 * kb + (lane & 15), s_k - 1);
+            const unsigned char* row =
+                base_k + (((int64_t)kphys[kb] << lb) + (key & bmask)) * slot_bytes +
+                (lane >> 4) * 8 * G::ESZ;
+#pragma unroll
+            for (int kc = 0; kc < G::NKC; ++kc) {
+                kreg[kb][kc] = *reinterpret_cast<const kword*>(row + 32 * G::ESZ * kc);
+            }
+        }
+        const int col = vcc * 16;
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int key = t * G::BN + vrow0 + i * G::RSTEP;
+            const int kc2 = min(key, s_k - 1);
+            const int64_t off = (((int64_t)vphys[i] << lb) + (kc2 & bmask)) * slot_bytes + col;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(base_v + off);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            vreg[i] = key < s_k ? w : z;
+        }
+    }
+    // the K operand of (kb, kc) in the Q type
+    __device__ __forceinline__ v8 kop(int kb, int kc) const {
+        if constexpr (FP8) {
+            const u32x2 lo = Q::cvt_fp8x4(kreg[kb][kc][0]);
+            const u32x2 hi = Q::cvt_fp8x4(kreg[kb][kc][1]);
+            return __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+            return __builtin_bit_cast(v8, kreg[kb][kc]);
+        }
+    }
+    __device__ __forceinline__ void store_v(unsigned short* v_lds) const {
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int row = vrow0 + i * G::RSTEP;
+            if (FP8) {
+                u32x4 v0, v1;
+                u32x2 t2;
+                t2 = Q::cvt_fp8x4(vreg[i][0]); v0[0] = t2[0]; v0[1] = t2[1];
+                t2 = Q::cvt_fp8x4(vreg[i][1]); v0[2] = t2[0]; v0[3] = t2[1];
+                t2 = Q::cvt_fp8x4(vreg[i][2]); v1[0] = t2[0]; v1[1] = t2[1];
+                t2 = Q::cvt_fp8x4(vreg[i][3]); v1[2] = t2[0]; v1[3] = t2[1];
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + vcc * 16]) = v0;
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + vcc * 16 + 8]) = v1;
+            } else {
+                *reinterpret_cast<u32x4*>(&v_lds[row * G::VSTR + vcc * 8]) = vreg[i];
+            }
+        }
+    }
+};
+
+// the value of lane l ^ 16
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+
+// per-lane offset (elements) of the first transposing V read of d block 0
+template <int D>
+__host__ __device__ inline int v16_frag_offset(int lane) {
+    const int G = lane >> 4, J = (lane & 15) >> 2, A = lane & 3;
+    return (4 * G + J) * (D + kVPad16) + 4 * A;
+}
+
+// S^T of one tile from the K operands in registers
+template <int D, typename QT, bool FP8>
+__device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8>& ld,
+                                          const typename QType<QT>::v8 (&qf)[D / 32],
+                                          f32x4 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x4{};
+#pragma unroll
+        for (int kc = 0; kc < D / 32; ++kc)
+            sacc[kb] = QType<QT>::mma16(ld.kop(kb, kc), qf[kc], sacc[kb]);
+    }
+}
+
+// transform, masks, online softmax and O^T += V^T P^T for one tile
+template <int D, typename QT, bool FP8, bool XFORM>
+__device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sacc)[2],
+                                             const unsigned short* __restrict__ v_lds,
+                                             f32x4 (&oacc)[D / 16], float& m_run, float& l_run,
+                                             int key0, bool need_mask, const RowCtx& rc, int grp,
+                                             int v_frag) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    typedef Geom16<D, FP8> G;
+    const bool softcap = XFORM && (p.flags & UA_FLAG_SOFTCAP);
+    const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
+    const float c = XFORM ? 1.0f : p.qk_scale_log2;
+    auto transform = [&](float x, int key) {
+        if (XFORM) {
+            x = softcap ? p.softcap_out - 2.0f * p.softcap_out *
+                                              __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
+                        : x * p.qk_scale_log2;
+            x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
+        }
+        return x;
+    };
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * kb + 4 * grp + i;
+            float sv = transform(sacc[kb][i], key);
+            if (need_mask) sv = ((key >= rc.kmin) & (key <= rc.kmax)) ? sv : -INFINITY;
+            sacc[kb][i] = sv;
+            mt = fmaxf(mt, sv);
+        }
+    mt = fmaxf(mt, xor16(mt));
+    mt = fmaxf(mt, xor32(mt)) * c;
+    // lazy reference max, as in the 32-row engine
+    if (__ballot(mt > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float m_base = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_base);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+    v8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        pf[j] = (QT)fast_exp2(__builtin_fmaf(sacc[j >> 2][j & 3], c, -m_use));
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[j], pf[j + 1], l_run);
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        const int off = v_frag + 16 * db;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off]);
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off + 16 * G::VSTR]);
+        u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        oacc[db] = Q::mma16(__builtin_bit_cast(v8, w), pf, oacc[db]);
+    }
+}
+
+// resident waves per SIMD the 16-row engine's registers allow
+constexpr int min_waves16(int d, bool fp8) {
+    return d <= 64 ? 4 : d <= 128 ? (fp8 ? 3 : 2) : (fp8 ? 2 : 1);
+}
+
+template <int D, typename QT, bool FP8, bool XFORM>
+__global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(UaKernelParams p) {
+    typedef QType<QT> Q;
+    typedef typename Q::v8 v8;
+    typedef Geom16<D, FP8> G;
+    constexpr int BN = G::BN;
+    static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
+
+    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * G::VSTR];
+
+    const int lane = threadIdx.x;
+    const int grp = lane >> 4;
+    const int64_t W = gridDim.x;
+    const int64_t j = blockIdx.x;
+    const int T = sk_total<BN>(p);
+    const int64_t A = j * T / W;
+    const int64_t B = (j + 1) * T / W;
+    if (A >= B) return;
+
+    int seq_first;
+    const int s0 = sk_locate<BN>(p, A, &seq_first);
+    SkPos pc = sk_pos<BN>(p, s0, 0, 0);
+    {
+        const int n = pc.t_end - pc.t_lo;
+        const int off = (int)(A - seq_first);
+        pc.h = off / n;
+        pc.t = pc.t_lo + (off - pc.h * n);
+    }
+    SkPos p1 = pc, p2 = pc;
+    if (A + 1 < B) p1 = sk_next<BN>(p, pc);
+    if (A + 2 < B) p2 = sk_next<BN>(p, p1);
+
+    const int lb = p.block_size_log2;
+    const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
+    const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
+    const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
+    auto bt_row = [&](const SkPos& q) { return p.block_table + (int64_t)q.s * p.bt_stride; };
+    auto hoff = [&](const SkPos& q) { return (int64_t)q.h * D * G::ESZ; };
+
+    Loader16<D, QT, FP8> ld;
+    ld.init(lane);
+    const int v_frag = v16_frag_offset<D>(lane);
+    ld.ids(bt_row(pc), pc.t, pc.s_k, lb, lane);
+    ld.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes, lane);
+    if (A + 1 < B) ld.ids(bt_row(p1), p1.t, p1.s_k, lb, lane);
+
+    RowInfo ri;
+    KeyRange kr;
+    v8 qf[G::NKC];
+    f32x4 oacc[G::NDB];
+    float m_run, l_run;
+    auto begin_pair = [&](const SkPos& q) {
+        ri = row_info(p, lane & 15, q.h, q.q_start, q.q_len, q.s_k, 0);
+        kr = key_range(p.flags, p.window, q.s_k, q.s_k - q.q_len, 0, q.q_len - 1);
+        const QT* qp = reinterpret_cast<const QT*>(p.q) + (int64_t)ri.tok * p.q_stride_tok +
+                       (int64_t)ri.head * D + 8 * grp;
+#pragma unroll
+        for (int k2 = 0; k2 < G::NKC; ++k2) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (ri.ok) w = *reinterpret_cast<const u32x4*>(qp + 32 * k2);
+            qf[k2] = __builtin_bit_cast(v8, w);
+        }
+        m_run = -INFINITY;
+        l_run = 0.0f;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) oacc[db] = f32x4{};
+    };
+    begin_pair(pc);
+
+    for (int64_t x = A; x < B; ++x) {
+        // this tile's V into LDS (the previous tile's reads are done: one
+        // wave, LDS operations in order), then the next tile's loads
+        ld.store_v(v_lds);
+        const int key0 = pc.t * BN;
+        const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
+        // QK consumes this tile's K operands before the next loads reuse them
+        f32x4 sacc[2];
+        qk_tile16<D, QT, FP8>(ld, qf, sacc);
+        if (x + 1 < B) {
+            ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
+            if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);
+        }
+        softmax_pv16<D, QT, FP8, XFORM>(p, sacc, v_lds, oacc, m_run, l_run, key0, need_mask, ri.rc,
+                                        grp, v_frag);
+        if (x + 1 == B || pc.t + 1 == pc.t_end) {
+            float l_tot = l_run + xor16(l_run);
+            l_tot += xor32(l_tot);
+            if (ri.ok) {
+                const int64_t slot = (int64_t)pc.s * p.num_kv_heads + pc.h + j;
+                const int64_t rid = slot * p.rows_used + (lane & 15);
+                float* wo = p.ws_o + rid * D + 4 * grp;
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+                    *reinterpret_cast<f32x4*>(wo + 16 * db) = oacc[db];
+                if (grp == 0) {
+                    p.ws_m[rid] = m_run;
+                    p.ws_l[rid] = l_tot;
+                }
+            }
+            if (x + 1 < B) begin_pair(p1);
+        }
+        pc = p1;
+        p1 = p2;
+        if (x + 3 < B) p2 = sk_next<BN>(p, p2);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp merge of split partials
 // ---------------------------------------------------------------------------
 //
@@ -1340,12 +1668,26 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
     if (l.events[0] && (e = hipEventRecord(l.events[0], st)) != hipSuccess) return e;
     const unsigned nb = (unsigned)((l.reduce_rows + 3) / 4);
     if (l.path == 3 && l.stream_k) {
-        if constexpr (NW == 1) {
-            const int workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>),
-                                         (int)kMaxStreamKWorkers);
-            p.sk_workers = workers;
-            hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>), dim3(workers), dim3(64), 0,
-                               st, p);
+        if constexpr (NW == 1 && BN == kSkTile) {
+            int workers = 0;
+            if (l.rows16) {
+                // built for d = 256 only (the plan asks for it there)
+                if constexpr (D == 256) {
+                    workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM>),
+                                       (int)kMaxStreamKWorkers);
+                    p.sk_workers = workers;
+                    hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM>), dim3(workers), dim3(64),
+                                       0, st, p);
+                } else {
+                    return hipErrorInvalidValue;
+                }
+            } else {
+                workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>),
+                                   (int)kMaxStreamKWorkers);
+                p.sk_workers = workers;
+                hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>), dim3(workers), dim3(64),
+                                   0, st, p);
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
             hipLaunchKernelGGL((ua_reduce_kernel<D, QT, true>), dim3(nb), dim3(256), 0, st, p,

@@ -60,6 +60,7 @@ struct UaLaunch {
     int kv_fp8;      // 1 when K/V are e4m3fn
     unsigned grid[3];
     int stream_k;    // split path: 1 = stream-K workers (single-wave geometry)
+    int rows16;      // stream-K with 16-row q-blocks (16x16x32 MFMA engine)
     int64_t reduce_rows;  // split path: total_q * H_q
     hipEvent_t events[3]; // optional: before attention, between kernels, at the end
 };
