@@ -1212,7 +1212,9 @@ struct Geom16 {
     static_assert(64 % CPR == 0 && BN % RSTEP == 0, "V tile rows must divide evenly");
 };
 
-template <int D, typename QT, bool FP8>
+// BIG: blocks of at least 16 keys, so each 16-key half of a tile lies in one
+// block and the V rows take their half's block id (no per-row table reads).
+template <int D, typename QT, bool FP8, bool BIG>
 struct Loader16 {
     typedef Geom16<D, FP8> G;
     typedef QType<QT> Q;
@@ -1221,7 +1223,7 @@ struct Loader16 {
     typedef typename std::conditional<FP8, u32x2, u32x4>::type kword;
     kword kreg[2][G::NKC];
     u32x4 vreg[G::NCH];
-    int kphys[2], vphys[G::NCH];
+    int kphys[2], vphys[BIG ? 1 : G::NCH];
     int vcc, vrow0;
 
     __device__ __forceinline__ void init(int lane) {
@@ -1234,10 +1236,12 @@ struct Loader16 {
             const int key = min(t * G::BN + 16 * kb + (lane & 15), s_k - 1);
             kphys[kb] = bt_row[key >> lb];
         }
+        if constexpr (!BIG) {
 #pragma unroll
-        for (int i = 0; i < G::NCH; ++i) {
-            const int key = min(t * G::BN + vrow0 + i * G::RSTEP, s_k - 1);
-            vphys[i] = bt_row[key >> lb];
+            for (int i = 0; i < G::NCH; ++i) {
+                const int key = min(t * G::BN + vrow0 + i * G::RSTEP, s_k - 1);
+                vphys[i] = bt_row[key >> lb];
+            }
         }
     }
     // K straight into operand registers (keys past S_k read slot S_k - 1 and
@@ -1261,7 +1265,9 @@ struct Loader16 {
         for (int i = 0; i < G::NCH; ++i) {
             const int key = t * G::BN + vrow0 + i * G::RSTEP;
             const int kc2 = min(key, s_k - 1);
-            const int64_t off = (((int64_t)vphys[i] << lb) + (kc2 & bmask)) * slot_bytes + col;
+            const int ph = BIG ? ((vrow0 + i * G::RSTEP) >= 16 ? kphys[1] : kphys[0])
+                               : vphys[BIG ? 0 : i];
+            const int64_t off = (((int64_t)ph << lb) + (kc2 & bmask)) * slot_bytes + col;
             const u32x4 w = *reinterpret_cast<const u32x4*>(base_v + off);
             const u32x4 z = {0u, 0u, 0u, 0u};
             vreg[i] = key < s_k ? w : z;
@@ -1308,8 +1314,8 @@ __host__ __device__ inline int v16_frag_offset(int lane) {
 }
 
 // S^T of one tile from the K operands in registers
-template <int D, typename QT, bool FP8>
-__device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8>& ld,
+template <int D, typename QT, bool FP8, bool BIG>
+__device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG>& ld,
                                           const typename QType<QT>::v8 (&qf)[D / 32],
                                           f32x4 (&sacc)[2]) {
 #pragma unroll
@@ -1389,7 +1395,7 @@ constexpr int min_waves16(int d, bool fp8) {
     return d <= 64 ? 4 : d <= 128 ? (fp8 ? 3 : 2) : (fp8 ? 2 : 1);
 }
 
-template <int D, typename QT, bool FP8, bool XFORM>
+template <int D, typename QT, bool FP8, bool XFORM, bool BIG>
 __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -1428,7 +1434,7 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
     auto bt_row = [&](const SkPos& q) { return p.block_table + (int64_t)q.s * p.bt_stride; };
     auto hoff = [&](const SkPos& q) { return (int64_t)q.h * D * G::ESZ; };
 
-    Loader16<D, QT, FP8> ld;
+    Loader16<D, QT, FP8, BIG> ld;
     ld.init(lane);
     const int v_frag = v16_frag_offset<D>(lane);
     ld.ids(bt_row(pc), pc.t, pc.s_k, lb, lane);
@@ -1466,7 +1472,7 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
         // QK consumes this tile's K operands before the next loads reuse them
         f32x4 sacc[2];
-        qk_tile16<D, QT, FP8>(ld, qf, sacc);
+        qk_tile16<D, QT, FP8, BIG>(ld, qf, sacc);
         if (x + 1 < B) {
             ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);
@@ -1673,11 +1679,19 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
             if (l.rows16) {
                 // built for d = 256 only (the plan asks for it there)
                 if constexpr (D == 256) {
-                    workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM>),
-                                       (int)kMaxStreamKWorkers);
-                    p.sk_workers = workers;
-                    hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM>), dim3(workers), dim3(64),
-                                       0, st, p);
+                    if (p.block_size_log2 >= 4) {
+                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM, true>),
+                                           (int)kMaxStreamKWorkers);
+                        p.sk_workers = workers;
+                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM, true>), dim3(workers),
+                                           dim3(64), 0, st, p);
+                    } else {
+                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM, false>),
+                                           (int)kMaxStreamKWorkers);
+                        p.sk_workers = workers;
+                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM, false>), dim3(workers),
+                                           dim3(64), 0, st, p);
+                    }
                 } else {
                     return hipErrorInvalidValue;
                 }
