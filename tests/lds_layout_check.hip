@@ -9,7 +9,9 @@
 //   * reads that the LDS serves together touch distinct banks;
 //   * the scalar-base lane offsets equal the per-lane slot addresses;
 //   * the 16-row decode engine's transposing V reads deliver V in the key
-//     order of the scores each lane holds, on distinct banks.
+//     order of the scores each lane holds, on distinct banks;
+//   * the stream-K partition names each tile's worker, and its partial slots
+//     are unique and inside the workspace.
 // Exit status 0 when all hold; the counts of violations are printed.
 #include "ua_attn_impl.h"
 
@@ -143,11 +145,62 @@ int check_v16() {
     return bad + conf;
 }
 
+// The stream-K partition: W workers split T flattened tiles into contiguous
+// ranges [jT/W, (j+1)T/W); sk_worker_of(x) must name the worker holding tile
+// x; and with random per-pair tile counts the partial slot p + j of every
+// ((sequence, kv-head) pair p, worker j) a worker touches is unique and below
+// (number of pairs) + W.  (N and G below are the pair and worker counts.)
+int check_stream_k() {
+    int bad = 0;
+    unsigned rng = 12345u;
+    auto next = [&]() { rng = rng * 1664525u + 1013904223u; return rng >> 8; };
+    for (int trial = 0; trial < 400; ++trial) {
+        const int N = 1 + next() % 70;
+        std::vector<int> n(N);
+        int64_t T = 0;
+        for (int s = 0; s < N; ++s) {
+            n[s] = next() % 5 == 0 ? 0 : (int)(next() % 300);
+            T += n[s];
+        }
+        const int64_t G = 1 + next() % 2100;
+        if (T == 0) continue;
+        std::vector<int> first(N + 1, 0);
+        for (int s = 0; s < N; ++s) first[s + 1] = first[s] + n[s];
+        std::vector<char> used((size_t)(N + G), 0);
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t A = g * T / G, B = (g + 1) * T / G;
+            for (int64_t x = A; x < B; ++x)
+                if (sk_worker_of(x, T, G) != g) ++bad;
+            if (A >= B) continue;
+            // sequences the group touches: those whose tile range meets [A, B)
+            for (int s = 0; s < N; ++s) {
+                if (n[s] == 0 || first[s + 1] <= A || first[s] >= B) continue;
+                const int64_t slot = s + g;
+                if (slot >= N + G || used[slot]) ++bad;
+                used[slot] = 1;
+            }
+        }
+        // a sequence's groups: from the group of its first tile to that of its last
+        for (int s = 0; s < N; ++s) {
+            if (n[s] == 0) continue;
+            const int g0 = sk_worker_of(first[s], T, G), g1 = sk_worker_of(first[s] + n[s] - 1, T, G);
+            for (int g = g0; g <= g1; ++g) {
+                const int64_t A = (int64_t)g * T / G, B = (int64_t)(g + 1) * T / G;
+                const bool live = A < B;
+                const bool meets = A < B && first[s + 1] > A && first[s] < B;
+                if (live != meets) ++bad;
+            }
+        }
+    }
+    std::printf("stream-K partition: violations %d\n", bad);
+    return bad;
+}
+
 }  // namespace
 
 int main() {
     const int bad = check_layout<64>() + check_layout<128>() + check_layout<256>() +
-                    check_v16<64>() + check_v16<128>() + check_v16<256>();
+                    check_v16<64>() + check_v16<128>() + check_v16<256>() + check_stream_k();
     std::printf(bad ? "FAIL\n" : "OK\n");
     return bad != 0;
 }

@@ -1026,7 +1026,7 @@ __device__ __forceinline__ int sk_locate(const UaKernelParams& p, int64_t x, int
 
 // worker j of W owns flattened tiles [floor(jT/W), floor((j+1)T/W)); the
 // worker holding tile x is ceil((x+1) W / T) - 1
-__device__ __forceinline__ int sk_worker_of(int64_t x, int64_t T, int64_t W) {
+__host__ __device__ inline int sk_worker_of(int64_t x, int64_t T, int64_t W) {
     return (int)(((x + 1) * W + T - 1) / T - 1);
 }
 
