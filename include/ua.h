@@ -111,6 +111,16 @@ typedef struct ua_problem* ua_problem_t;
  *               kernel, so a caller can time the kernels one by one.  On a
  *               class-split run (ua_plan_info.class_split) [0] precedes both
  *               launches and [1], [2] follow both, reduces included.
+ *  lse          optional device f32 [total_q, H_q] (token-major, NULL to skip):
+ *               the natural-log log-sum-exp of each row's softmax denominator,
+ *               ln(sum over visible keys of e^{s_k} (+ e^{sink_h})), with s_k
+ *               the scores after scale, softcap and ALiBi; -inf for a row
+ *               with no visible key.  This is the per-row statistic that
+ *               merges independent attention results over disjoint key sets
+ *               (section 5 of the unified page's re-base, in natural log).
+ *               The denominator sums the same 16-bit-rounded p as O, so it
+ *               agrees with the exact value to about 2^-9 relative (LSE to
+ *               about 2e-3 absolute).  4-byte aligned.
  * Device metadata is trusted: 0 <= q_len <= S_k <= max_seqlen_k, and used
  * block-table entries lie in [0, num_blocks). */
 typedef struct ua_run_args {
@@ -133,6 +143,7 @@ typedef struct ua_run_args {
     int64_t q_stride_tok;
     int64_t o_stride_tok;
     void* timing_events[3];
+    float* lse;
 } ua_run_args_t;
 
 /* Which kernel strategy a run takes (section 6 of the unified page). */

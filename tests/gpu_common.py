@@ -16,18 +16,22 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_hip(w, extra_flags=0, batch=None, ua=None, repeat=1, split_segment_tiles=0):
-    """Run the HIP path on workload w; returns (O as float64 numpy, plan)."""
+def run_hip(w, extra_flags=0, batch=None, ua=None, repeat=1, split_segment_tiles=0, lse=False):
+    """Run the HIP path on workload w; returns (O as float64 numpy, plan), and
+    the row LSE [total_q, H_q] as a third item when `lse` is set."""
     if batch is None:
         batch = D.DeviceBatch(w)
     if ua is None:
         ua = D.UnifiedAttention(D.problem_desc(w, extra_flags,
                                                split_segment_tiles=split_segment_tiles))
     plan = ua.plan(w)
+    lse_buf = batch.lse_buffer() if lse else None
     for _ in range(repeat):
-        ua.run(batch)
+        ua.run(batch, lse=lse_buf)
     torch.cuda.synchronize()
     o = batch.output().float().cpu().numpy().astype(np.float64)
+    if lse:
+        return o, plan, lse_buf.cpu().numpy().astype(np.float64)
     return o, plan
 
 

@@ -105,6 +105,7 @@ BAD_ARGS = [
     (dict(q=None), B.UA_ERR_INVALID_ARG, "null required"),
     (dict(cu_seqlens_q=None), B.UA_ERR_INVALID_ARG, "null required"),
     (dict(o=(1 << 20) + 2), B.UA_ERR_INVALID_ARG, "aligned"),
+    (dict(lse=(1 << 20) + 2), B.UA_ERR_INVALID_ARG, "lse must be 4-byte aligned"),
 ]
 
 

@@ -184,6 +184,48 @@ def test_small_block_sizes(d, b):
         _full_check(w, force, f"b={b}/d={d}/{force}")
 
 
+LSE_TOL = 4e-3  # the denominator sums 16-bit-rounded p: about 2^-9 relative
+
+LSE_CASES = [
+    # (name, workload maker, force)
+    ("2d_ring", lambda: W.random_small(900, num_seqs=5, max_q=70, max_k=300, num_q_heads=8,
+                                       num_kv_heads=2, head_dim=128, block_size=16), "2d"),
+    ("seg_ring_sinks_softcap", lambda: W.random_small(901, num_seqs=5, max_q=70, max_k=300,
+                                                      num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                                      block_size=16, use_sinks=True,
+                                                      softcap=8.0), "3d_seg"),
+    ("2d_registers_fp8_alibi", lambda: W.random_small(902, num_seqs=4, max_q=50, max_k=260,
+                                                      num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                                      block_size=16, kv_dtype=W.DT_FP8_E4M3,
+                                                      use_alibi=True), "2d"),
+    ("stream_k_32rows_window", lambda: W.build(
+        "lse_sk32", 903, np.ones(30, np.int64), np.random.default_rng(903).integers(1, 900, 30),
+        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, window=200,
+        use_sinks=True), "auto"),
+    ("stream_k_16rows_fp8_d256", lambda: W.build(
+        "lse_sk16", 904, np.ones(30, np.int64), np.random.default_rng(904).integers(1, 900, 30),
+        num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=32, kv_dtype=W.DT_FP8_E4M3,
+        q_dtype=W.DT_F16, use_sinks=True), "auto"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(LSE_CASES)))
+def test_row_lse_matches_oracle(i):
+    """The optional row log-sum-exp output on each path (2D ring and register
+    kernels, the segmented split, both stream-K engines) against the oracle's
+    natural-log LSE, sinks included."""
+    name, make, force = LSE_CASES[i]
+    w = make()
+    o, plan, lse = run_hip(w, FORCE[force], split_segment_tiles=SEG_TILES.get(force, 0), lse=True)
+    ref_o, ref_lse = oracle.attention(w, return_lse=True)
+    compare(o, ref_o, f"lse/{name} O")
+    both_inf = np.isinf(lse) & np.isinf(ref_lse) & (np.sign(lse) == np.sign(ref_lse))
+    err = np.where(both_inf, 0.0, np.abs(lse - ref_lse))
+    say(f"  lse/{name}: path={plan.path} stream_k={plan.stream_k} max_abs={float(np.max(err)):.3e}")
+    assert not np.isnan(lse).any()
+    assert float(np.max(err)) <= LSE_TOL
+
+
 @pytest.mark.parametrize("force", ["auto", "2d", "3d"])
 def test_prefill_ragged(force):
     """Self-attention prefill with lengths that are not tile multiples."""

@@ -81,6 +81,7 @@ class ua_run_args_t(ctypes.Structure):
         ("q_stride_tok", ctypes.c_int64),
         ("o_stride_tok", ctypes.c_int64),
         ("timing_events", ctypes.c_void_p * 3),
+        ("lse", ctypes.c_void_p),
     ]
 
 

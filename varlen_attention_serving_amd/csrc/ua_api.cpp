@@ -402,6 +402,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         return fail(UA_ERR_INVALID_ARG, "sinks flagged but sinks is null");
     if (((uintptr_t)a->q | (uintptr_t)a->o | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache) & 15)
         return fail(UA_ERR_INVALID_ARG, "q, o, k_cache and v_cache must be 16-byte aligned");
+    if ((uintptr_t)a->lse & 3) return fail(UA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
 
     Plan pl;
     ua_status_t st = make_plan(*p, a->num_seqs, a->total_q, a->max_seqlen_q, a->max_seqlen_k, &pl);
@@ -417,6 +418,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.cu_q = a->cu_seqlens_q;
     base.slopes = (d.flags & UA_FLAG_ALIBI) ? a->alibi_slopes : nullptr;
     base.sinks = (d.flags & UA_FLAG_SINKS) ? a->sinks : nullptr;
+    base.lse = a->lse;
     base.q_stride_tok = a->q_stride_tok;
     base.o_stride_tok = a->o_stride_tok;
     base.kv_slot_stride = (int64_t)d.num_kv_heads * d.head_dim;

@@ -66,6 +66,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// natural-log LSE of a row from its reference max m (log2 units) and the
+// denominator l relative to it; -inf when nothing was visible
+__device__ __forceinline__ float row_lse(float m, float l) {
+    return l > 0.0f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+}
 constexpr int kKPad = 8;   // K LDS row padding (elements)
 constexpr int kVPad = 32;  // V LDS row padding (elements)
 // Register budget: at least two resident waves per SIMD, so one wave's MFMAs
@@ -746,6 +753,7 @@ __device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowIn
         const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
         write_partial<D>(p, rid, half, oacc, m_run, l_tot);
     } else {
+        if (p.lse && half == 0) p.lse[(int64_t)ri.tok * p.num_q_heads + ri.head] = row_lse(m_run, l_tot);
         const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
         QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)ri.tok * p.o_stride_tok +
                  (int64_t)ri.head * D + 4 * half;
@@ -1557,6 +1565,7 @@ __device__ __forceinline__ void merge_partials(const UaKernelParams& p, int64_t 
         mx = bm;
     }
     const float inv = L > 0.0f ? p.out_scale / L : 0.0f;
+    if (p.lse && lane == 0) p.lse[(int64_t)tok * p.num_q_heads + head] = row_lse(mx, L);
     QT* dst = reinterpret_cast<QT*>(p.o) + (int64_t)tok * p.o_stride_tok + (int64_t)head * D +
               lane * EPL;
 #pragma unroll

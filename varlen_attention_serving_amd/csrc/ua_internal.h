@@ -15,6 +15,7 @@ struct UaKernelParams {
     const int32_t* cu_q;
     const float* slopes;      // ALiBi slopes (natural units) or null
     const float* sinks;       // sink logits (natural units) or null
+    float* lse;               // optional [total_q, H_q] natural-log row LSE (NULL: skip)
     float* ws_o;              // split partials: un-normalised o  [rows, NS, D]
     float* ws_m;              //                 running max (log2 units) [rows, NS]
     float* ws_l;              //                 denominator           [rows, NS]

@@ -65,10 +65,17 @@ class DeviceBatch:
         """O viewed in its storage dtype (bf16 / f16)."""
         return self.o.view(_TORCH_VIEW[self.w.q_dtype])
 
-    def run_args(self, workspace=None) -> B.ua_run_args_t:
+    def lse_buffer(self) -> torch.Tensor:
+        """A float32 [total_q, H_q] buffer for the optional row LSE output."""
+        if getattr(self, "lse", None) is None:
+            self.lse = torch.full((self.w.total_q, self.w.num_q_heads), float("nan"),
+                                  dtype=torch.float32, device=self.o.device)
+        return self.lse
+
+    def run_args(self, workspace=None, lse=None) -> B.ua_run_args_t:
         w = self.w
         ptr = lambda t: None if t is None else t.data_ptr()
-        return B.ua_run_args_t(
+        return B.ua_run_args_t(lse=ptr(lse),
             q=ptr(self.q), k_cache=ptr(self.k), v_cache=ptr(self.v), o=ptr(self.o),
             block_table=ptr(self.block_table), seq_lens=ptr(self.seq_lens),
             cu_seqlens_q=ptr(self.cu_seqlens_q), alibi_slopes=ptr(self.alibi_slopes),
@@ -95,9 +102,9 @@ class UnifiedAttention:
         return B.ua_query_plan(self.handle, w.num_seqs, w.total_q, w.max_seqlen_q,
                                w.max_seqlen_k)
 
-    def run(self, batch: DeviceBatch, stream=None) -> None:
+    def run(self, batch: DeviceBatch, stream=None, lse=None) -> None:
         s = torch.cuda.current_stream() if stream is None else stream
-        B.ua_run(self.handle, batch.run_args(self.workspace), s.cuda_stream)
+        B.ua_run(self.handle, batch.run_args(self.workspace, lse), s.cuda_stream)
 
     def close(self):
         if self.handle:
