@@ -43,6 +43,9 @@ class UaoProblem(ctypes.Structure):
         ("softcap", ctypes.c_double),
         ("k_scale", ctypes.c_double),
         ("v_scale", ctypes.c_double),
+        ("use_qq_bias", ctypes.c_int32),
+        ("qq_bias_stride", ctypes.c_int32),
+        ("qq_bias", ctypes.c_void_p),
     ]
 
 
@@ -97,7 +100,8 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def _problem(w) -> UaoProblem:
-    return UaoProblem(
+    qq = getattr(w, "qq_bias", None)
+    p = UaoProblem(
         num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
         head_dim=w.head_dim, block_size=w.block_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
         causal=int(w.causal), use_softcap=int(w.softcap > 0), use_alibi=int(w.use_alibi),
@@ -105,6 +109,13 @@ def _problem(w) -> UaoProblem:
         block_table_stride=int(w.block_table.shape[1]),
         q_stride_tok=int(w.num_q_heads * w.head_dim), scale=float(w.scale),
         softcap=float(w.softcap), k_scale=float(w.k_scale), v_scale=float(w.v_scale))
+    if qq is not None:
+        qq = np.ascontiguousarray(qq, dtype=np.float32)
+        p._qq_keep = qq  # the struct holds a raw pointer: keep the array alive with it
+        p.use_qq_bias = 1
+        p.qq_bias_stride = int(qq.shape[1])
+        p.qq_bias = qq.ctypes.data
+    return p
 
 
 def _arrays(w):

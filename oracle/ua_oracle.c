@@ -18,10 +18,12 @@
  *   1. scale    x_k  = tau * <Q_i, K_k>
  *   2. softcap  x_k  = c * tanh(x_k / c)                           (if enabled)
  *   3. ALiBi    x_k += slope_h * (k - ctx)                         (if enabled)
- *   4. causal   k > q_abs              -> masked                   (if enabled)
- *   5. window   k <= q_abs - W         -> masked (W keys remain)   (if enabled)
- *   6. sinks    one extra softmax column with logit sink_h and no value row
- *   7. O_i = sum_{k visible} e^{x_k - m} V_k / Z,
+ *   4. QQ-bias  x_k += bias[i][k - ctx]  for k >= ctx (the query    (if enabled)
+ *               section); one matrix shared by all heads and sequences
+ *   5. causal   k > q_abs              -> masked                   (if enabled)
+ *   6. window   k <= q_abs - W         -> masked (W keys remain)   (if enabled)
+ *   7. sinks    one extra softmax column with logit sink_h and no value row
+ *   then O_i = sum_{k visible} e^{x_k - m} V_k / Z,
  *      Z   = sum_{k visible} e^{x_k - m} + [sinks] e^{sink_h - m},
  *      m   = max over the visible x_k and the sink logit;  O_i = 0 if nothing
  *      is visible.
@@ -65,6 +67,9 @@ typedef struct uao_problem {
     double softcap;
     double k_scale;
     double v_scale;
+    int32_t use_qq_bias;
+    int32_t qq_bias_stride;     /* elements between rows of qq_bias */
+    const float* qq_bias;       /* [q_local][k_local] over the query section */
 } uao_problem;
 
 /* ---- exact decoders ----------------------------------------------------- */
@@ -158,7 +163,10 @@ static int uao_row(const uao_problem* p, const void* q, const void* k_cache, con
         if (p->use_softcap) x = p->softcap * tanh(x / p->softcap);
         /* 3. ALiBi */
         if (p->use_alibi) x += (double)slopes[head] * (double)(k - ctx);
-        /* 4. causal, 5. window */
+        /* 4. QQ-bias, for keys inside the query section (k >= ctx) */
+        if (p->use_qq_bias && k >= ctx)
+            x += (double)p->qq_bias[i * p->qq_bias_stride + (k - ctx)];
+        /* 5. causal, 6. window */
         int visible = 1;
         if (p->causal && k > q_abs) visible = 0;
         if (p->use_window && k < q_abs - p->window + 1 - UAO_WINDOW_EXTRA_KEY) visible = 0;
@@ -169,7 +177,7 @@ static int uao_row(const uao_problem* p, const void* q, const void* k_cache, con
             if (x > m) m = x;
         }
     }
-    /* 6. sinks take part in the max and the denominator only */
+    /* 7. sinks take part in the max and the denominator only */
     double sink = p->use_sinks ? (double)sinks[head] : 0.0;
     if (p->use_sinks && sink > m) m = sink;
 
@@ -178,7 +186,7 @@ static int uao_row(const uao_problem* p, const void* q, const void* k_cache, con
         if (lse) *lse = p->use_sinks ? sink : -INFINITY;
         return 0;
     }
-    /* 7. softmax-weighted sum of V */
+    /* the softmax-weighted sum of V */
     double z = p->use_sinks ? exp(sink - m) : 0.0;
     for (int64_t k = 0; k < sk; ++k) {
         if (!vis[k]) continue;

@@ -60,6 +60,10 @@ def brute_force(w, window_extra_key=0):
                 s_mat = w.softcap * np.tanh(s_mat / w.softcap)
             if w.use_alibi:
                 s_mat = s_mat + float(w.alibi_slopes[h]) * (kpos - ctx)
+            if getattr(w, "qq_bias", None) is not None:
+                # the query section: keys ctx .. S_k - 1, biased by bias[i, k - ctx]
+                s_mat = s_mat.copy()
+                s_mat[:, ctx:] += w.qq_bias[:ql, :ql].astype(np.float64)
             s_mat = np.where(allowed, s_mat, -np.inf)
             cols = [s_mat]
             if w.use_sinks:

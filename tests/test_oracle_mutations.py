@@ -29,6 +29,10 @@ MUTANTS = {
     "v_scale_dropped": ("out[e] += w * uao_load_kv(v_cache, v_off + e, p->kv_dtype, p->v_scale);",
                         "out[e] += w * uao_load_kv(v_cache, v_off + e, p->kv_dtype, 1.0);"),
     "ctx_ignored": ("const int64_t q_abs = ctx + i;", "const int64_t q_abs = i;"),
+    "qq_bias_transposed": ("p->qq_bias[i * p->qq_bias_stride + (k - ctx)]",
+                           "p->qq_bias[(k - ctx) * p->qq_bias_stride + i]"),
+    "qq_bias_section_off_by_one": ("if (p->use_qq_bias && k >= ctx)",
+                                   "if (p->use_qq_bias && k > ctx)"),
 }
 
 # Cases drawn from the pinned workloads: brute force is the independent check.
@@ -37,6 +41,7 @@ CASES = [
     dict(softcap=2.0, use_alibi=True, window=9, use_sinks=True),
     dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True, use_sinks=True, window=11),
     dict(softcap=0.5),
+    dict(use_qq_bias=True, causal=False),
 ]
 
 

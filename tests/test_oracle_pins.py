@@ -69,6 +69,8 @@ FLAG_CASES = [
     dict(q_dtype=W.DT_F16, kv_dtype=W.DT_F16, use_sinks=True),
     dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True, use_sinks=True, window=11),
     dict(kv_dtype=W.DT_FP8_E4M3),
+    dict(use_qq_bias=True),
+    dict(use_qq_bias=True, causal=False, use_alibi=True, softcap=2.0, window=9, use_sinks=True),
 ]
 
 
@@ -154,6 +156,28 @@ def test_window_and_alibi_vs_sdpa_float_mask(causal):
         assert _rel(o[t0:t0 + q_len], _sdpa_seq(w, s, float_mask=mask)) < 1e-11
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_qq_bias_vs_sdpa_float_mask(causal):
+    """QQ-bias is an additive float mask over the query section: keys
+    ctx .. S_k - 1 of local query row i get bias[i, k - ctx]."""
+    rng = np.random.default_rng(14)
+    sk = rng.integers(20, 120, size=4, endpoint=True)
+    ql = np.minimum(sk, rng.integers(1, 30, size=4, endpoint=True))
+    w = W.build("qq", 14, ql, sk, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                causal=causal, rng=rng, use_qq_bias=True)
+    o = oracle.attention(w)
+    for s in range(w.num_seqs):
+        t0, q_len, s_k = int(w.cu_seqlens_q[s]), int(w.q_lens[s]), int(w.seq_lens[s])
+        ctx = s_k - q_len
+        bias = np.zeros((q_len, s_k))
+        bias[:, ctx:] = w.qq_bias[:q_len, :q_len]
+        if causal:
+            qa = ctx + np.arange(q_len)[:, None]
+            bias = np.where(np.arange(s_k)[None, :] <= qa, bias, -np.inf)
+        mask = torch.from_numpy(np.broadcast_to(bias, (w.num_q_heads, q_len, s_k)).copy())
+        assert _rel(o[t0:t0 + q_len], _sdpa_seq(w, s, float_mask=mask)) < 1e-11
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
@@ -211,6 +235,29 @@ def test_identical_keys_with_alibi_give_geometric_weights():
             wt = r ** (kk - kk.max())
             expect = (wt[:, None] * v[kk, 0, :]).sum(0) / wt.sum()
             assert np.max(np.abs(o[i, h] - expect)) < 1e-12
+
+
+def test_identical_keys_with_qq_bias_weigh_the_query_section():
+    """With every key equal, the weights are e^bias[i, k - ctx] on the query
+    section and 1 on the context: the bias's row is the query, its column
+    the key (an asymmetric matrix tells the two apart)."""
+    rng = np.random.default_rng(24)
+    w = _identical_keys(W.build("ikq", 24, [5, 3], [17, 3], num_q_heads=2, num_kv_heads=1,
+                                head_dim=32, block_size=4, causal=False, use_qq_bias=True,
+                                rng=rng), rng)
+    assert np.max(np.abs(w.qq_bias - w.qq_bias.T)) > 0.1
+    o = oracle.attention(w)
+    for s in range(2):
+        _, v = dense_kv(w, s)
+        q_len, s_k = int(w.q_lens[s]), int(w.seq_lens[s])
+        ctx = s_k - q_len
+        for i in range(q_len):
+            wt = np.ones(s_k)
+            wt[ctx:] = np.exp(w.qq_bias[i, :q_len].astype(np.float64))
+            expect = (wt[:, None] * v[:, 0, :]).sum(0) / wt.sum()
+            t = int(w.cu_seqlens_q[s]) + i
+            for h in range(2):
+                assert np.max(np.abs(o[t, h] - expect)) < 1e-12
 
 
 def test_identical_keys_with_sinks():

@@ -72,6 +72,7 @@ class Workload:
     sinks: Optional[np.ndarray]         # float32 [H_q] or None
     k_scale: float = 1.0
     v_scale: float = 1.0
+    qq_bias: Optional[np.ndarray] = None  # float32 [max_q, max_q] query-section bias, or None
 
     @property
     def num_seqs(self) -> int:
@@ -209,7 +210,7 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
           causal: bool = True, softcap: float = 0.0, window: int = 0, use_alibi: bool = False,
           use_sinks: bool = False, scale: Optional[float] = None, num_blocks: Optional[int] = None,
           rng: Optional[np.random.Generator] = None, poison: bool = True,
-          table_slack_cols: int = 0) -> Workload:
+          table_slack_cols: int = 0, use_qq_bias: bool = False) -> Workload:
     """Draw one workload.  ``q_lens``/``seq_lens`` are already drawn by the caller
     (from ``rng`` when random) so the lengths come first in the draw order."""
     if rng is None:
@@ -262,6 +263,9 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
 
     slopes = alibi_slopes(num_q_heads) if use_alibi else None
     sinks = rng.standard_normal(num_q_heads, dtype=np.float32) if use_sinks else None
+    # one query-section bias matrix for every head and sequence, drawn last
+    mq = max(1, int(np.max(q_lens)) if len(q_lens) else 1)
+    qq_bias = rng.standard_normal((mq, mq), dtype=np.float32) if use_qq_bias else None
 
     if poison:
         nan = _NAN_BITS[kv_dtype]
@@ -284,7 +288,7 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
         scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
         q_lens=q_lens, seq_lens=seq_lens, cu_seqlens_q=cu, block_table=block_table,
         num_blocks=num_blocks, q=q, k_cache=k_cache, v_cache=v_cache, alibi_slopes=slopes,
-        sinks=sinks, k_scale=k_scale, v_scale=v_scale)
+        sinks=sinks, k_scale=k_scale, v_scale=v_scale, qq_bias=qq_bias)
 
 
 # ----------------------------------------------------------------------------
