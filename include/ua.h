@@ -55,6 +55,7 @@ enum {
     UA_FLAG_ALIBI = 1u << 2,    /* s += slope_h (k - ctx) */
     UA_FLAG_WINDOW = 1u << 3,   /* keep the last `window` keys: q_abs - W < k <= q_abs */
     UA_FLAG_SINKS = 1u << 4,    /* per-head logit joins the softmax with no value row */
+    UA_FLAG_QQ_BIAS = 1u << 5,  /* bias[q_local][k - ctx] on keys of the query section */
     UA_FLAG_FORCE_2D = 1u << 8, /* testing/benchmarking: bypass the shape rule */
     UA_FLAG_FORCE_3D = 1u << 9
 };
@@ -101,6 +102,13 @@ typedef struct ua_problem* ua_problem_t;
  *               q_len key positions (ctx = S_k - q_len).
  *  alibi_slopes device f32 [H_q] when UA_FLAG_ALIBI, else NULL.
  *  sinks        device f32 [H_q] (natural-log logits) when UA_FLAG_SINKS, else NULL.
+ *  qq_bias      device f32 matrix when UA_FLAG_QQ_BIAS, else NULL: step 4 of
+ *               section 1 of the unified page adds qq_bias[i * qq_bias_stride +
+ *               (k - ctx)] (natural-log units, after ALiBi, before the masks)
+ *               to the score of local query row i and key k when k >= ctx,
+ *               i.e. for keys inside the sequence's query section.  One matrix
+ *               serves all heads and sequences; it must cover max_seqlen_q rows
+ *               and columns (qq_bias_stride >= max_seqlen_q), 4-byte aligned.
  *  workspace    device, >= ua_workspace_size() bytes, 256-byte aligned; used
  *               only by the split-KV path (may be NULL if that size is 0).
  *  num_seqs, total_q, max_seqlen_q, max_seqlen_k are host copies of the
@@ -144,6 +152,8 @@ typedef struct ua_run_args {
     int64_t o_stride_tok;
     void* timing_events[3];
     float* lse;
+    const float* qq_bias;
+    int32_t qq_bias_stride;
 } ua_run_args_t;
 
 /* Which kernel strategy a run takes (section 6 of the unified page). */

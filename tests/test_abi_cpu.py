@@ -123,10 +123,22 @@ def test_invalid_run_arguments_are_rejected(i):
 
 
 def test_flagged_inputs_need_their_pointers():
-    for flag, text in ((B.UA_FLAG_ALIBI, "alibi_slopes"), (B.UA_FLAG_SINKS, "sinks")):
+    for flag, text in ((B.UA_FLAG_ALIBI, "alibi_slopes"), (B.UA_FLAG_SINKS, "sinks"),
+                       (B.UA_FLAG_QQ_BIAS, "qq_bias is null")):
         h = B.ua_create_problem(_desc(flags=B.UA_FLAG_CAUSAL | flag))
         with pytest.raises(B.UaError, match=text):
             B.ua_run(h, _args(), None)
+        B.ua_destroy_problem(h)
+
+
+def test_qq_bias_must_cover_the_query_rows():
+    h = B.ua_create_problem(_desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_QQ_BIAS))
+    try:
+        with pytest.raises(B.UaError, match="qq_bias_stride"):
+            B.ua_run(h, _args(qq_bias=1 << 20, qq_bias_stride=3), None)  # max_seqlen_q = 4
+        with pytest.raises(B.UaError, match="qq_bias must be 4-byte aligned"):
+            B.ua_run(h, _args(qq_bias=(1 << 20) + 2, qq_bias_stride=4), None)
+    finally:
         B.ua_destroy_problem(h)
 
 

@@ -184,6 +184,28 @@ def test_small_block_sizes(d, b):
         _full_check(w, force, f"b={b}/d={d}/{force}")
 
 
+QQ_CASES = [
+    # (name, shape (H_q, H_k, d, b), flags, force)
+    ("2d_ring", (8, 2, 128, 16), dict(), "2d"),
+    ("seg_ring_noncausal_alibi", (8, 2, 64, 16), dict(causal=False, use_alibi=True), "3d_seg"),
+    ("2d_registers_fp8_sinks", (8, 2, 128, 32), dict(kv_dtype=W.DT_FP8_E4M3, use_sinks=True), "2d"),
+    ("d256_softcap_window", (16, 4, 256, 32), dict(softcap=20.0, window=40), "auto"),
+    ("stream_k_chunks", (32, 8, 128, 16), dict(use_sinks=True), "3d"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(QQ_CASES)))
+def test_qq_bias(i):
+    """QQ-bias on the query section ([UA] section 1, step 4) on the 2D ring and
+    register kernels, the segmented split, d = 256 and stream-K (short
+    chunks)."""
+    name, (hq, hk, d, b), flags, force = QQ_CASES[i]
+    max_q = 3 if force == "3d" and name.startswith("stream_k") else 60
+    w = W.random_small(950 + i, num_seqs=5, max_q=max_q, max_k=260, num_q_heads=hq,
+                       num_kv_heads=hk, head_dim=d, block_size=b, use_qq_bias=True, **flags)
+    _full_check(w, force, f"qq/{name}/{force}")
+
+
 LSE_TOL = 4e-3  # the denominator sums 16-bit-rounded p: about 2^-9 relative
 
 LSE_CASES = [

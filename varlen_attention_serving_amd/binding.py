@@ -25,6 +25,7 @@ UA_FLAG_SOFTCAP = 1 << 1
 UA_FLAG_ALIBI = 1 << 2
 UA_FLAG_WINDOW = 1 << 3
 UA_FLAG_SINKS = 1 << 4
+UA_FLAG_QQ_BIAS = 1 << 5
 UA_FLAG_FORCE_2D = 1 << 8
 UA_FLAG_FORCE_3D = 1 << 9
 
@@ -82,6 +83,8 @@ class ua_run_args_t(ctypes.Structure):
         ("o_stride_tok", ctypes.c_int64),
         ("timing_events", ctypes.c_void_p * 3),
         ("lse", ctypes.c_void_p),
+        ("qq_bias", ctypes.c_void_p),
+        ("qq_bias_stride", ctypes.c_int32),
     ]
 
 

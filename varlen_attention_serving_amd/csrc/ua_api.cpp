@@ -286,7 +286,7 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
         return fail(UA_ERR_UNSUPPORTED, "kv_dtype %d must equal q_dtype or be fp8 e4m3",
                     d.kv_dtype);
     const uint32_t known = UA_FLAG_CAUSAL | UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_WINDOW |
-                           UA_FLAG_SINKS | UA_FLAG_FORCE_2D | UA_FLAG_FORCE_3D;
+                           UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_FORCE_2D | UA_FLAG_FORCE_3D;
     if (d.flags & ~known) return fail(UA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags & ~known);
     if ((d.flags & UA_FLAG_FORCE_2D) && (d.flags & UA_FLAG_FORCE_3D))
         return fail(UA_ERR_INVALID_ARG, "FORCE_2D and FORCE_3D are exclusive");
@@ -403,6 +403,14 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     if (((uintptr_t)a->q | (uintptr_t)a->o | (uintptr_t)a->k_cache | (uintptr_t)a->v_cache) & 15)
         return fail(UA_ERR_INVALID_ARG, "q, o, k_cache and v_cache must be 16-byte aligned");
     if ((uintptr_t)a->lse & 3) return fail(UA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (d.flags & UA_FLAG_QQ_BIAS) {
+        if (!a->qq_bias) return fail(UA_ERR_INVALID_ARG, "QQ-bias flagged but qq_bias is null");
+        if ((uintptr_t)a->qq_bias & 3)
+            return fail(UA_ERR_INVALID_ARG, "qq_bias must be 4-byte aligned");
+        if (a->qq_bias_stride < a->max_seqlen_q)
+            return fail(UA_ERR_INVALID_ARG, "qq_bias_stride %d below max_seqlen_q %d",
+                        a->qq_bias_stride, a->max_seqlen_q);
+    }
 
     Plan pl;
     ua_status_t st = make_plan(*p, a->num_seqs, a->total_q, a->max_seqlen_q, a->max_seqlen_k, &pl);
@@ -419,6 +427,8 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.slopes = (d.flags & UA_FLAG_ALIBI) ? a->alibi_slopes : nullptr;
     base.sinks = (d.flags & UA_FLAG_SINKS) ? a->sinks : nullptr;
     base.lse = a->lse;
+    base.qq_bias = (d.flags & UA_FLAG_QQ_BIAS) ? a->qq_bias : nullptr;
+    base.qq_stride = a->qq_bias_stride;
     base.q_stride_tok = a->q_stride_tok;
     base.o_stride_tok = a->o_stride_tok;
     base.kv_slot_stride = (int64_t)d.num_kv_heads * d.head_dim;

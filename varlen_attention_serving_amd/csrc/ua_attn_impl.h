@@ -472,7 +472,16 @@ struct RowCtx {
     int kmin;    // first visible key
     int kmax;    // last visible key
     float slope2;  // ALiBi slope in log2 units (0 when off)
+    int qloc;    // the row's local query index (clamped into the section)
+    int qlast;   // q_len - 1 of the row's sequence
 };
+
+// QQ-bias of (row, key) in log2 units for a key of the query section; the
+// column is clamped so keys past S_k (masked) read inside the matrix
+__device__ __forceinline__ float qq_bias2(const UaKernelParams& p, const RowCtx& rc, int key) {
+    const int kl = min(key - rc.ctx, rc.qlast);
+    return p.qq_bias[(int64_t)rc.qloc * p.qq_stride + kl] * kLog2e;
+}
 
 // Rows of one q-block: pos_local = r / g, head_local = r % g.
 struct RowInfo {
@@ -494,6 +503,8 @@ __device__ __forceinline__ RowInfo row_info(const UaKernelParams& p, int r, int 
     ri.rc.kmax = (p.flags & UA_FLAG_CAUSAL) ? min(q_abs, s_k - 1) : s_k - 1;
     ri.rc.kmin = (p.flags & UA_FLAG_WINDOW) ? q_abs - p.window + 1 : 0;
     ri.rc.slope2 = (p.flags & UA_FLAG_ALIBI) ? p.slopes[ri.head] * kLog2e : 0.0f;
+    ri.rc.qloc = min(p0 + pr, q_len - 1);
+    ri.rc.qlast = q_len - 1;
     return ri;
 }
 
@@ -549,6 +560,9 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
     const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
     const float c = XFORM ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
+    // QQ-bias only on tiles that reach the query section (ctx is the same for
+    // every row of a q-block, so the test is uniform)
+    const bool qq = XFORM && (p.flags & UA_FLAG_QQ_BIAS) && key0 + BN > rc.ctx;
     auto transform = [&](float x, int key) {
         if (XFORM) {
             // c tanh(y) = c - 2c / (1 + e^{2y}), with e^{2y} = 2^{x * softcap_in2}: saturates
@@ -557,6 +571,7 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
                                               __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
                         : x * p.qk_scale_log2;
             x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
+            if (qq && key >= rc.ctx) x += qq_bias2(p, rc, key);
         }
         return x;
     };
@@ -643,7 +658,7 @@ __device__ __forceinline__ void pv_tile(const unsigned short* __restrict__ v_lds
     }
 }
 
-// One tile: scores, scale -> softcap -> ALiBi -> masks (log2 units), the
+// One tile: scores, scale -> softcap -> ALiBi -> QQ-bias -> masks (log2 units), the
 // online-softmax update, then O^T += V^T P^T.  key0 is the tile's first key
 // position.  XFORM = false compiles the plain scale for problems without
 // softcap and ALiBi.
@@ -1348,12 +1363,14 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
     const bool softcap = XFORM && (p.flags & UA_FLAG_SOFTCAP);
     const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
     const float c = XFORM ? 1.0f : p.qk_scale_log2;
+    const bool qq = XFORM && (p.flags & UA_FLAG_QQ_BIAS) && key0 + G::BN > rc.ctx;
     auto transform = [&](float x, int key) {
         if (XFORM) {
             x = softcap ? p.softcap_out - 2.0f * p.softcap_out *
                                               __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
                         : x * p.qk_scale_log2;
             x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
+            if (qq && key >= rc.ctx) x += qq_bias2(p, rc, key);
         }
         return x;
     };
@@ -1774,7 +1791,8 @@ hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream
 
 template <int D, typename QT, bool FP8>
 hipError_t launch_xform(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
-    if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI)) return launch_geometry<D, QT, FP8, true>(p, l, st);
+    if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_QQ_BIAS))
+        return launch_geometry<D, QT, FP8, true>(p, l, st);
     return launch_geometry<D, QT, FP8, false>(p, l, st);
 }
 

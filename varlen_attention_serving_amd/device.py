@@ -25,6 +25,8 @@ def problem_desc(w, extra_flags: int = 0, max_total_q=None, max_seqlen_k=None,
         flags |= B.UA_FLAG_WINDOW
     if w.use_sinks:
         flags |= B.UA_FLAG_SINKS
+    if getattr(w, "qq_bias", None) is not None:
+        flags |= B.UA_FLAG_QQ_BIAS
     return B.ua_problem_desc_t(
         num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
         block_size=w.block_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, flags=flags,
@@ -59,6 +61,7 @@ class DeviceBatch:
             np.ascontiguousarray(a, dtype=np.float32)).to(dev)
         self.alibi_slopes = f32(w.alibi_slopes)
         self.sinks = f32(w.sinks)
+        self.qq_bias = f32(getattr(w, "qq_bias", None))
         self.o = torch.zeros_like(self.q)
 
     def output(self) -> torch.Tensor:
@@ -84,7 +87,9 @@ class DeviceBatch:
             workspace_bytes=0 if workspace is None else workspace.numel(),
             num_seqs=w.num_seqs, max_seqlen_q=w.max_seqlen_q, total_q=w.total_q,
             max_seqlen_k=w.max_seqlen_k, block_table_stride=int(w.block_table.shape[1]),
-            q_stride_tok=w.num_q_heads * w.head_dim, o_stride_tok=w.num_q_heads * w.head_dim)
+            q_stride_tok=w.num_q_heads * w.head_dim, o_stride_tok=w.num_q_heads * w.head_dim,
+            qq_bias=ptr(self.qq_bias),
+            qq_bias_stride=0 if self.qq_bias is None else int(self.qq_bias.shape[1]))
 
 
 class UnifiedAttention:
