@@ -55,7 +55,10 @@ def algorithmic_work(w):
     esz_kv = 1 if w.kv_dtype == 2 else 2
     kv_bytes = int(visited.sum()) * w.num_kv_heads * w.head_dim * esz_kv * 2
     q_bytes = w.total_q * w.num_q_heads * w.head_dim * 2
-    meta = blocks * 4 + w.num_seqs * 4 + (w.num_seqs + 1) * 4
+    # paged: one table entry per visited block, S_k and cu_seqlens_q; dense:
+    # cu_seqlens_q and cu_seqlens_k only
+    meta = (2 * (w.num_seqs + 1) * 4 if getattr(w, "dense", False)
+            else blocks * 4 + w.num_seqs * 4 + (w.num_seqs + 1) * 4)
     meta += (w.num_q_heads * 4 if w.use_alibi else 0) + (w.num_q_heads * 4 if w.use_sinks else 0)
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     dense_flops = 4 * w.head_dim * w.num_q_heads * int(
@@ -174,7 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
-                             "variant_mix", "tiny_varlen"])
+                             "variant_mix", "tiny_varlen", "dense_prefill"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scratch buffer between timed steps (outside the "
@@ -319,6 +322,7 @@ def main():
             "num_seqs": w.num_seqs, "total_q": w.total_q, "max_seqlen_k": w.max_seqlen_k,
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size,
+            "kv_layout": "dense (cu_seqlens_k)" if w.dense else "paged (block table)",
             "path": {2: "2d", 3: "3d-split-kv"}[plan.path], "segments": plan.num_segments,
             "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
             "dense_equivalent_flops": work["dense_flops"],

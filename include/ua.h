@@ -56,6 +56,7 @@ enum {
     UA_FLAG_WINDOW = 1u << 3,   /* keep the last `window` keys: q_abs - W < k <= q_abs */
     UA_FLAG_SINKS = 1u << 4,    /* per-head logit joins the softmax with no value row */
     UA_FLAG_QQ_BIAS = 1u << 5,  /* bias[q_local][k - ctx] on keys of the query section */
+    UA_FLAG_DENSE_KV = 1u << 6, /* K/V packed per sequence: rows cu_seqlens_k[s] + k */
     UA_FLAG_FORCE_2D = 1u << 8, /* testing/benchmarking: bypass the shape rule */
     UA_FLAG_FORCE_3D = 1u << 9
 };
@@ -66,7 +67,8 @@ typedef struct ua_problem_desc {
     int32_t num_q_heads;         /* H_q > 0 */
     int32_t num_kv_heads;        /* H_k > 0, H_q % H_k == 0, g = H_q / H_k <= 128 */
     int32_t head_dim;            /* d in {64, 128, 256} */
-    int32_t block_size;          /* b in {16, 32, 64} (KV positions per physical block) */
+    int32_t block_size;          /* b: power of two <= 1024 (KV positions per physical
+                                    block); 1 with UA_FLAG_DENSE_KV */
     int32_t q_dtype;             /* UA_DTYPE_BF16 or UA_DTYPE_F16 */
     int32_t kv_dtype;            /* q_dtype or UA_DTYPE_FP8_E4M3 */
     uint32_t flags;              /* UA_FLAG_* */
@@ -102,6 +104,15 @@ typedef struct ua_problem* ua_problem_t;
  *               q_len key positions (ctx = S_k - q_len).
  *  alibi_slopes device f32 [H_q] when UA_FLAG_ALIBI, else NULL.
  *  sinks        device f32 [H_q] (natural-log logits) when UA_FLAG_SINKS, else NULL.
+ *  cu_seqlens_k device int32 [num_seqs + 1] when UA_FLAG_DENSE_KV, else NULL:
+ *               the packed varlen layout of the dense sibling (section 8 of the
+ *               unified page; the varlen variant of the dense-prefill page)
+ *               stores key k of sequence s, kv-head h at row cu_seqlens_k[s] + k
+ *               of k_cache / v_cache [rows, H_k, d], and S_k = cu_seqlens_k[s+1]
+ *               - cu_seqlens_k[s].  The problem's block_size must be 1 and
+ *               num_blocks counts rows.  block_table, block_table_stride and
+ *               seq_lens are not read (may be NULL / 0).  Queries keep their
+ *               own cu_seqlens_q: q_len < S_k is a chunk at the sequence's end.
  *  qq_bias      device f32 matrix when UA_FLAG_QQ_BIAS, else NULL: step 4 of
  *               section 1 of the unified page adds qq_bias[i * qq_bias_stride +
  *               (k - ctx)] (natural-log units, after ALiBi, before the masks)
@@ -154,6 +165,7 @@ typedef struct ua_run_args {
     float* lse;
     const float* qq_bias;
     int32_t qq_bias_stride;
+    const int32_t* cu_seqlens_k;
 } ua_run_args_t;
 
 /* Which kernel strategy a run takes (section 6 of the unified page). */

@@ -65,6 +65,7 @@ BAD_DESCS = [
     (dict(kv_dtype=B.UA_DTYPE_FP8_E4M3, k_scale=0.0), B.UA_ERR_INVALID_ARG, "k_scale"),
     (dict(num_blocks=0), B.UA_ERR_INVALID_ARG, "num_blocks"),
     (dict(max_seqlen_k=2048, max_blocks_per_seq=64), B.UA_ERR_INVALID_ARG, "max_blocks_per_seq"),
+    (dict(flags=B.UA_FLAG_DENSE_KV), B.UA_ERR_INVALID_ARG, "needs block_size 1"),
 ]
 
 
@@ -138,6 +139,32 @@ def test_qq_bias_must_cover_the_query_rows():
             B.ua_run(h, _args(qq_bias=1 << 20, qq_bias_stride=3), None)  # max_seqlen_q = 4
         with pytest.raises(B.UaError, match="qq_bias must be 4-byte aligned"):
             B.ua_run(h, _args(qq_bias=(1 << 20) + 2, qq_bias_stride=4), None)
+    finally:
+        B.ua_destroy_problem(h)
+
+
+def _dense_desc(extra=0):
+    return _desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_DENSE_KV | extra, block_size=1,
+                 num_blocks=4096, max_blocks_per_seq=0)
+
+
+def test_dense_layout_needs_cu_seqlens_k_and_no_table():
+    no_table = dict(block_table=None, seq_lens=None, block_table_stride=0)
+    h = B.ua_create_problem(_dense_desc())
+    try:
+        with pytest.raises(B.UaError, match="cu_seqlens_k"):
+            B.ua_run(h, _args(**no_table), None)
+        with pytest.raises(B.UaError, match="cu_seqlens_k"):
+            B.ua_run(h, _args(cu_seqlens_k=(1 << 20) + 2, **no_table), None)
+    finally:
+        B.ua_destroy_problem(h)
+    # with cu_seqlens_k given, the table arguments are not validated: a forced
+    # split run gets as far as the workspace check
+    h = B.ua_create_problem(_dense_desc(B.UA_FLAG_FORCE_3D))
+    try:
+        with pytest.raises(B.UaError) as e:
+            B.ua_run(h, _args(cu_seqlens_k=1 << 20, **no_table), None)
+        assert e.value.status == B.UA_ERR_WORKSPACE
     finally:
         B.ua_destroy_problem(h)
 

@@ -206,6 +206,38 @@ def test_qq_bias(i):
     _full_check(w, force, f"qq/{name}/{force}")
 
 
+DENSE_CASES = [
+    # (name, shape (H_q, H_k, d, paged b), workload flags, force, max_q)
+    ("2d_ring", (8, 2, 128, 16), dict(), "2d", 300),
+    ("2d_ring_d64_window_alibi", (8, 2, 64, 16), dict(window=50, use_alibi=True), "2d", 90),
+    ("seg_ring_softcap_sinks", (8, 2, 128, 16), dict(softcap=20.0, use_sinks=True), "3d_seg", 90),
+    ("2d_registers_fp8_qq", (8, 2, 128, 32), dict(kv_dtype=W.DT_FP8_E4M3, use_qq_bias=True),
+     "2d", 90),
+    ("d256_noncausal", (16, 4, 256, 32), dict(causal=False), "auto", 60),
+    ("stream_k_decode", (32, 8, 128, 16), dict(use_sinks=True), "3d", 1),
+    ("stream_k_16rows_d256_fp8", (16, 2, 256, 32), dict(kv_dtype=W.DT_FP8_E4M3, window=70),
+     "auto", 1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DENSE_CASES)))
+def test_dense_layout(i):
+    """K/V packed per sequence and addressed through cu_seqlens_k (the dense
+    sibling of [UA] section 8) on every path: the 2D ring and register
+    kernels, the segmented split, d = 256 and both stream-K engines.  The
+    oracle reads the same rows through the identity table of block size 1;
+    the same batch in its paged layout gives bitwise the same output."""
+    name, (hq, hk, d, b), flags, force, max_q = DENSE_CASES[i]
+    w = W.random_small(960 + i, num_seqs=6, max_q=max_q, max_k=400, num_q_heads=hq,
+                       num_kv_heads=hk, head_dim=d, block_size=b, **flags)
+    wd = W.to_dense(w)
+    o, plan = _full_check(wd, force, f"dense/{name}/{force}")
+    paged, plan_p = run_hip(w, FORCE[force], split_segment_tiles=SEG_TILES.get(force, 0))
+    assert (plan.path, plan.stream_k, plan.class_split) == \
+        (plan_p.path, plan_p.stream_k, plan_p.class_split)
+    assert np.array_equal(o, paged)
+
+
 LSE_TOL = 4e-3  # the denominator sums 16-bit-rounded p: about 2^-9 relative
 
 LSE_CASES = [
@@ -319,7 +351,7 @@ def test_nan_poison_in_unused_blocks_and_tails_never_reaches_output():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["decode_batch", "chunked_prefill_mix", "long_prefill",
-                                  "variant_mix"])
+                                  "variant_mix", "dense_prefill"])
 def test_named_workload_full_size(name):
     say(f"[gpu] {name}: generating")
     w = W.NAMED[name]()

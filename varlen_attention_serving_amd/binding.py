@@ -26,6 +26,7 @@ UA_FLAG_ALIBI = 1 << 2
 UA_FLAG_WINDOW = 1 << 3
 UA_FLAG_SINKS = 1 << 4
 UA_FLAG_QQ_BIAS = 1 << 5
+UA_FLAG_DENSE_KV = 1 << 6
 UA_FLAG_FORCE_2D = 1 << 8
 UA_FLAG_FORCE_3D = 1 << 9
 
@@ -85,6 +86,7 @@ class ua_run_args_t(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("qq_bias", ctypes.c_void_p),
         ("qq_bias_stride", ctypes.c_int32),
+        ("cu_seqlens_k", ctypes.c_void_p),
     ]
 
 

@@ -286,7 +286,8 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
         return fail(UA_ERR_UNSUPPORTED, "kv_dtype %d must equal q_dtype or be fp8 e4m3",
                     d.kv_dtype);
     const uint32_t known = UA_FLAG_CAUSAL | UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_WINDOW |
-                           UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_FORCE_2D | UA_FLAG_FORCE_3D;
+                           UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_DENSE_KV | UA_FLAG_FORCE_2D |
+                           UA_FLAG_FORCE_3D;
     if (d.flags & ~known) return fail(UA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags & ~known);
     if ((d.flags & UA_FLAG_FORCE_2D) && (d.flags & UA_FLAG_FORCE_3D))
         return fail(UA_ERR_INVALID_ARG, "FORCE_2D and FORCE_3D are exclusive");
@@ -306,14 +307,21 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     if (d.max_total_q > INT32_MAX) return fail(UA_ERR_UNSUPPORTED, "max_total_q exceeds 2^31");
     if (d.split_segment_tiles < 0)
         return fail(UA_ERR_INVALID_ARG, "split_segment_tiles must be >= 0");
-    if ((int64_t)d.max_blocks_per_seq * d.block_size < d.max_seqlen_k)
+    const bool dense = (d.flags & UA_FLAG_DENSE_KV) != 0;
+    if (dense && d.block_size != 1)
+        return fail(UA_ERR_INVALID_ARG, "the dense K/V layout needs block_size 1 (got %d)",
+                    d.block_size);
+    if (!dense && (int64_t)d.max_blocks_per_seq * d.block_size < d.max_seqlen_k)
         return fail(UA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size < max_seqlen_k");
+    if (dense && d.max_seqlen_k > (1 << 30))
+        return fail(UA_ERR_UNSUPPORTED, "dense max_seqlen_k above 2^30");
 
     ua_problem* P = new (std::nothrow) ua_problem;
     if (!P) return fail(UA_ERR_INVALID_ARG, "out of host memory");
     P->d = d;
     P->group = g;
-    P->log2_block = ilog2(d.block_size);
+    // the kernels see a dense sequence as one block of 2^30 rows
+    P->log2_block = dense ? 30 : ilog2(d.block_size);
     P->fp8 = d.kv_dtype == UA_DTYPE_FP8_E4M3;
     // split workspace: enough segments for the smallest tile (32 keys) and the
     // minimum segment length at the maxima, capped at 2 GiB (a larger batch
@@ -389,13 +397,16 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         return fail(UA_ERR_INVALID_ARG, "token strides must be >= H_q * head_dim");
     if (a->q_stride_tok % 8 || a->o_stride_tok % 8)
         return fail(UA_ERR_INVALID_ARG, "token strides must be multiples of 8 elements");
-    if (a->block_table_stride < cdiv(a->max_seqlen_k, d.block_size) ||
-        a->block_table_stride > std::max(d.max_blocks_per_seq, 1))
+    const bool dense = (d.flags & UA_FLAG_DENSE_KV) != 0;
+    if (!dense && (a->block_table_stride < cdiv(a->max_seqlen_k, d.block_size) ||
+                   a->block_table_stride > std::max(d.max_blocks_per_seq, 1)))
         return fail(UA_ERR_INVALID_ARG, "block_table_stride %d outside [ceil(max_seqlen_k/b), %d]",
                     a->block_table_stride, d.max_blocks_per_seq);
-    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->block_table || !a->seq_lens ||
-        !a->cu_seqlens_q)
+    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->cu_seqlens_q ||
+        (!dense && (!a->block_table || !a->seq_lens)))
         return fail(UA_ERR_INVALID_ARG, "null required device pointer");
+    if (dense && (!a->cu_seqlens_k || ((uintptr_t)a->cu_seqlens_k & 3)))
+        return fail(UA_ERR_INVALID_ARG, "dense K/V need a 4-byte aligned cu_seqlens_k");
     if ((d.flags & UA_FLAG_ALIBI) && !a->alibi_slopes)
         return fail(UA_ERR_INVALID_ARG, "ALiBi flagged but alibi_slopes is null");
     if ((d.flags & UA_FLAG_SINKS) && !a->sinks)
@@ -421,8 +432,9 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.k = a->k_cache;
     base.v = a->v_cache;
     base.o = a->o;
-    base.block_table = a->block_table;
-    base.seq_lens = a->seq_lens;
+    base.block_table = dense ? nullptr : a->block_table;
+    base.seq_lens = dense ? nullptr : a->seq_lens;
+    base.cu_k = dense ? a->cu_seqlens_k : nullptr;
     base.cu_q = a->cu_seqlens_q;
     base.slopes = (d.flags & UA_FLAG_ALIBI) ? a->alibi_slopes : nullptr;
     base.sinks = (d.flags & UA_FLAG_SINKS) ? a->sinks : nullptr;
@@ -437,7 +449,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.num_kv_heads = d.num_kv_heads;
     base.group = p->group;
     base.block_size_log2 = p->log2_block;
-    base.bt_stride = a->block_table_stride;
+    base.bt_stride = dense ? 1 : a->block_table_stride;
     base.flags = d.flags;
     base.window = (d.flags & UA_FLAG_WINDOW) ? d.window : 0;
     const float kscale = p->fp8 ? d.k_scale : 1.0f;

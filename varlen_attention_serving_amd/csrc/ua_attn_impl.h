@@ -716,6 +716,26 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // 2D query-tile kernel and the segmented 3D split-KV kernel
 // ---------------------------------------------------------------------------
 
+// The one block id of the dense K/V layout: a whole sequence is one block
+// (block_size_log2 = 30) whose rows start at the sequence's row offset.
+__constant__ int32_t kDenseBlockId[1] = {0};
+
+// S_k of sequence s.  Paged: clamped to the block table's width, since a
+// longer length would read past the table (a violated precondition).  Dense:
+// the difference of cu_seqlens_k.
+__device__ __forceinline__ int seq_keys(const UaKernelParams& p, int s) {
+    if (p.cu_k) return p.cu_k[s + 1] - p.cu_k[s];
+    return min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
+}
+// Byte offset of sequence s's first K/V row (dense layout; 0 when paged).
+__device__ __forceinline__ int64_t seq_kv_bytes(const UaKernelParams& p, int s, int64_t slot_bytes) {
+    return p.cu_k ? (int64_t)p.cu_k[s] * slot_bytes : 0;
+}
+// Block-table row of sequence s (the single zero id when dense).
+__device__ __forceinline__ const int32_t* table_row(const UaKernelParams& p, int s) {
+    return p.block_table ? p.block_table + (int64_t)s * p.bt_stride : kDenseBlockId;
+}
+
 // The q-block (and, split, the run of its KV tiles) a workgroup owns; false
 // when it owns nothing.
 struct QBlockWork {
@@ -737,9 +757,7 @@ __device__ __forceinline__ bool qblock_work(const UaKernelParams& p, int slot, i
     if (local >= blocks) return false;
     w.p0 = (blocks - 1 - local) * p.block_q;
     if (p.class_mode == 2 && w.q_len <= p.small_block_q) return false;  // the decode kernel's rows
-    // S_k beyond the block table's width would read past the table (a violated
-    // precondition); clamp so the gather stays inside it.
-    w.s_k = min(p.seq_lens[w.s], p.bt_stride << p.block_size_log2);
+    w.s_k = seq_keys(p, w.s);
     const int p_last = min(w.p0 + p.block_q, w.q_len) - 1;
     w.kr = key_range(p.flags, p.window, w.s_k, w.s_k - w.q_len, w.p0, p_last);
     w.t_lo = w.kr.lo / BN;
@@ -830,12 +848,11 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
     for (int dt = 0; dt < G::NDT; ++dt) oacc[dt] = f32x16{};
 
     const int lb = p.block_size_log2;
-    const int32_t* bt = p.block_table + (int64_t)s * p.bt_stride;
+    const int32_t* bt = table_row(p, s);
     const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
-    const unsigned char* base_k =
-        reinterpret_cast<const unsigned char*>(p.k) + (int64_t)hk * D * G::ESZ;
-    const unsigned char* base_v =
-        reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * G::ESZ;
+    const int64_t kv0 = seq_kv_bytes(p, s, slot_bytes) + (int64_t)hk * D * G::ESZ;
+    const unsigned char* base_k = reinterpret_cast<const unsigned char*>(p.k) + kv0;
+    const unsigned char* base_v = reinterpret_cast<const unsigned char*>(p.v) + kv0;
     KvLoader<D, NW, BN, QT, FP8> ld;
     ld.init(tid);
     const Frag fr = padded_frag<D>(lane);
@@ -909,10 +926,11 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
 
     const int lb = p.block_size_log2;
-    const const_i32_ptr bt = (const_i32_ptr)(p.block_table + (int64_t)qb.s * p.bt_stride);
+    const const_i32_ptr bt = (const_i32_ptr)table_row(p, qb.s);
     const uint64_t slot_bytes = (uint64_t)p.kv_slot_stride * 2;
-    const unsigned char* base_k = reinterpret_cast<const unsigned char*>(p.k) + (int64_t)hk * D * 2;
-    const unsigned char* base_v = reinterpret_cast<const unsigned char*>(p.v) + (int64_t)hk * D * 2;
+    const int64_t kv0 = seq_kv_bytes(p, qb.s, (int64_t)slot_bytes) + (int64_t)hk * D * 2;
+    const unsigned char* base_k = reinterpret_cast<const unsigned char*>(p.k) + kv0;
+    const unsigned char* base_v = reinterpret_cast<const unsigned char*>(p.v) + kv0;
     LdsCopy<D> cp;
     cp.init(wave, lane, (uint32_t)slot_bytes);
     const Frag fr = swizzled_frag<D>(lane);
@@ -995,7 +1013,7 @@ __device__ __forceinline__ SeqLane seq_lane(const UaKernelParams& p, int s) {
     if (s >= p.num_seqs) return r;
     r.q_start = p.cu_q[s];
     r.q_len = p.cu_q[s + 1] - r.q_start;
-    r.s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
+    r.s_k = seq_keys(p, s);
     if (r.q_len <= 0) return r;
     if (p.class_mode == 1 && r.q_len > p.small_block_q) return r;  // another kernel's rows
     const KeyRange kr = key_range(p.flags, p.window, r.s_k, r.s_k - r.q_len, 0, r.q_len - 1);
@@ -1056,6 +1074,7 @@ __host__ __device__ inline int sk_worker_of(int64_t x, int64_t T, int64_t W) {
 // A position in the flattened tile space with the facts of its pair.
 struct SkPos {
     int s, h, t, t_lo, t_end, q_start, q_len, s_k;
+    int kv_row;  // the sequence's first K/V row (dense layout; 0 when paged)
 };
 
 template <int BN>
@@ -1065,6 +1084,7 @@ __device__ __forceinline__ SkPos sk_pos(const UaKernelParams& p, int s, int h, i
     r.s = s; r.h = h; r.t = t;
     r.t_lo = q.t_lo; r.t_end = q.t_lo + q.n;
     r.q_start = q.q_start; r.q_len = q.q_len; r.s_k = q.s_k;
+    r.kv_row = p.cu_k ? p.cu_k[s] : 0;
     return r;
 }
 
@@ -1086,6 +1106,7 @@ __device__ __forceinline__ SkPos sk_next(const UaKernelParams& p, const SkPos& c
     while (q.n == 0 && s + 1 < p.num_seqs) q = seq_lane<BN>(p, ++s);
     r.s = s; r.h = 0; r.t = q.t_lo; r.t_lo = q.t_lo; r.t_end = q.t_lo + q.n;
     r.q_start = q.q_start; r.q_len = q.q_len; r.s_k = q.s_k;
+    r.kv_row = p.cu_k ? p.cu_k[s] : 0;
     return r;
 }
 
@@ -1144,8 +1165,8 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
     const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
     const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
     const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
-    auto bt_row = [&](const SkPos& q) { return p.block_table + (int64_t)q.s * p.bt_stride; };
-    auto hoff = [&](const SkPos& q) { return (int64_t)q.h * D * G::ESZ; };
+    auto bt_row = [&](const SkPos& q) { return table_row(p, q.s); };
+    auto hoff = [&](const SkPos& q) { return q.kv_row * slot_bytes + (int64_t)q.h * D * G::ESZ; };
 
     KvLoader<D, 1, BN, QT, FP8> ld;
     ld.init(lane);
@@ -1456,8 +1477,8 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
     const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
     const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
     const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
-    auto bt_row = [&](const SkPos& q) { return p.block_table + (int64_t)q.s * p.bt_stride; };
-    auto hoff = [&](const SkPos& q) { return (int64_t)q.h * D * G::ESZ; };
+    auto bt_row = [&](const SkPos& q) { return table_row(p, q.s); };
+    auto hoff = [&](const SkPos& q) { return q.kv_row * slot_bytes + (int64_t)q.h * D * G::ESZ; };
 
     Loader16<D, QT, FP8, BIG> ld;
     ld.init(lane);
@@ -1656,7 +1677,7 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const int q_start = p.cu_q[s];
         const int q_len = p.cu_q[s + 1] - q_start;
         if (p.class_mode == 2 && q_len <= p.small_block_q) return;  // the decode kernel's rows
-        const int s_k = min(p.seq_lens[s], p.bt_stride << p.block_size_log2);
+        const int s_k = seq_keys(p, s);
         const int ctx = s_k - q_len;
         const int p0 = ((tok - q_start) / p.block_q) * p.block_q;
         const int p_last = min(p0 + p.block_q, q_len) - 1;

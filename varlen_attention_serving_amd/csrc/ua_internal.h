@@ -17,6 +17,7 @@ struct UaKernelParams {
     const float* sinks;       // sink logits (natural units) or null
     float* lse;               // optional [total_q, H_q] natural-log row LSE (NULL: skip)
     const float* qq_bias;     // [q_local][k_local] query-section bias (QQ_BIAS flag)
+    const int32_t* cu_k;      // dense K/V: first row of each sequence (else NULL)
     int qq_stride;
     float* ws_o;              // split partials: un-normalised o  [rows, NS, D]
     float* ws_m;              //                 running max (log2 units) [rows, NS]

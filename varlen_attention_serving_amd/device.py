@@ -27,6 +27,8 @@ def problem_desc(w, extra_flags: int = 0, max_total_q=None, max_seqlen_k=None,
         flags |= B.UA_FLAG_SINKS
     if getattr(w, "qq_bias", None) is not None:
         flags |= B.UA_FLAG_QQ_BIAS
+    if getattr(w, "dense", False):
+        flags |= B.UA_FLAG_DENSE_KV
     return B.ua_problem_desc_t(
         num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
         block_size=w.block_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, flags=flags,
@@ -54,8 +56,11 @@ class DeviceBatch:
             self.k = as16(w.k_cache)
             self.v = as16(w.v_cache)
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-        self.block_table = i32(w.block_table)
-        self.seq_lens = i32(w.seq_lens)
+        self.dense = bool(getattr(w, "dense", False))
+        # the dense layout is addressed by cu_seqlens_k alone: no table, no S_k array
+        self.block_table = None if self.dense else i32(w.block_table)
+        self.seq_lens = None if self.dense else i32(w.seq_lens)
+        self.cu_seqlens_k = i32(w.cu_seqlens_k) if self.dense else None
         self.cu_seqlens_q = i32(w.cu_seqlens_q)
         f32 = lambda a: None if a is None else torch.from_numpy(
             np.ascontiguousarray(a, dtype=np.float32)).to(dev)
@@ -86,7 +91,9 @@ class DeviceBatch:
             workspace=None if workspace is None else workspace.data_ptr(),
             workspace_bytes=0 if workspace is None else workspace.numel(),
             num_seqs=w.num_seqs, max_seqlen_q=w.max_seqlen_q, total_q=w.total_q,
-            max_seqlen_k=w.max_seqlen_k, block_table_stride=int(w.block_table.shape[1]),
+            max_seqlen_k=w.max_seqlen_k,
+            block_table_stride=0 if self.dense else int(w.block_table.shape[1]),
+            cu_seqlens_k=ptr(self.cu_seqlens_k),
             q_stride_tok=w.num_q_heads * w.head_dim, o_stride_tok=w.num_q_heads * w.head_dim,
             qq_bias=ptr(self.qq_bias),
             qq_bias_stride=0 if self.qq_bias is None else int(self.qq_bias.shape[1]))

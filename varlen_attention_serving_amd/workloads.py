@@ -73,6 +73,13 @@ class Workload:
     k_scale: float = 1.0
     v_scale: float = 1.0
     qq_bias: Optional[np.ndarray] = None  # float32 [max_q, max_q] query-section bias, or None
+    dense: bool = False                  # keys contiguous per sequence (block size 1, identity)
+
+    @property
+    def cu_seqlens_k(self) -> np.ndarray:
+        cu = np.zeros(self.num_seqs + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(self.seq_lens)
+        return cu
 
     @property
     def num_seqs(self) -> int:
@@ -210,9 +217,11 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
           causal: bool = True, softcap: float = 0.0, window: int = 0, use_alibi: bool = False,
           use_sinks: bool = False, scale: Optional[float] = None, num_blocks: Optional[int] = None,
           rng: Optional[np.random.Generator] = None, poison: bool = True,
-          table_slack_cols: int = 0, use_qq_bias: bool = False) -> Workload:
+          table_slack_cols: int = 0, use_qq_bias: bool = False, dense: bool = False) -> Workload:
     """Draw one workload.  ``q_lens``/``seq_lens`` are already drawn by the caller
-    (from ``rng`` when random) so the lengths come first in the draw order."""
+    (from ``rng`` when random) so the lengths come first in the draw order.
+    ``dense`` lays every sequence's keys out contiguously, in sequence order
+    (block size 1, identity table): the dense K/V layout [total_k, H_k, d]."""
     if rng is None:
         rng = np.random.default_rng(seed)
     q_lens = np.asarray(q_lens, dtype=np.int32)
@@ -232,7 +241,9 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
     max_blocks = int(nb_seq.max()) + table_slack_cols if n else 1
     max_blocks = max(max_blocks, 1)
 
-    perm = rng.permutation(num_blocks).astype(np.int32)
+    if dense and b != 1:
+        raise ValueError("a dense layout has block size 1")
+    perm = (np.arange(num_blocks) if dense else rng.permutation(num_blocks)).astype(np.int32)
     block_table = np.full((n, max_blocks), -1, dtype=np.int32)
     off = 0
     for s in range(n):
@@ -288,7 +299,35 @@ def build(name: str, seed: int, q_lens, seq_lens, *, num_q_heads: int, num_kv_he
         scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
         q_lens=q_lens, seq_lens=seq_lens, cu_seqlens_q=cu, block_table=block_table,
         num_blocks=num_blocks, q=q, k_cache=k_cache, v_cache=v_cache, alibi_slopes=slopes,
-        sinks=sinks, k_scale=k_scale, v_scale=v_scale, qq_bias=qq_bias)
+        sinks=sinks, k_scale=k_scale, v_scale=v_scale, qq_bias=qq_bias, dense=dense)
+
+
+
+def to_dense(w: Workload) -> Workload:
+    """The same batch with its K/V rows packed per sequence (the dense layout):
+    row cu_seqlens_k[s] + k holds the cached row of key k.  Pure data movement;
+    the slack rows past the last sequence are NaN."""
+    if w.dense:
+        return w
+    n, b = w.num_seqs, w.block_size
+    cu_k = w.cu_seqlens_k
+    total = int(cu_k[-1])
+    rows = total + 16
+    shape = (rows, 1) + w.k_cache.shape[2:]
+    nan = _NAN_BITS[w.kv_dtype]
+    k = np.full(shape, nan, dtype=w.k_cache.dtype)
+    v = np.full(shape, nan, dtype=w.v_cache.dtype)
+    table = np.full((n, max(1, int(w.seq_lens.max()) if n else 1)), -1, dtype=np.int32)
+    for s in range(n):
+        sk = int(w.seq_lens[s])
+        key = np.arange(sk)
+        phys = w.block_table[s, key // b]
+        k[cu_k[s]:cu_k[s] + sk, 0] = w.k_cache[phys, key % b]
+        v[cu_k[s]:cu_k[s] + sk, 0] = w.v_cache[phys, key % b]
+        table[s, :sk] = cu_k[s] + key
+    return Workload(**{**w.__dict__, "name": w.name + "_dense", "block_size": 1,
+                       "num_blocks": rows, "block_table": table, "k_cache": k, "v_cache": v,
+                       "dense": True})
 
 
 # ----------------------------------------------------------------------------
@@ -344,12 +383,21 @@ def _spec_variant_mix(seed):
                         use_sinks=True, scale=1.0 / 16.0))
 
 
+def _spec_dense_prefill(seed):
+    """The dense sibling's shape: 1 sequence S_q = S_k = 8192, H_q=128, H_k=8,
+    d=128, bf16, causal, K/V packed per sequence (no block table)."""
+    return dict(q_lens=[8192], seq_lens=[8192], rng=None,
+                kw=dict(num_q_heads=128, num_kv_heads=8, head_dim=128, block_size=1,
+                        dense=True))
+
+
 NAMED_SPECS = {
     "tiny_varlen": (1, _spec_tiny_varlen),
     "decode_batch": (2, _spec_decode_batch),
     "chunked_prefill_mix": (3, _spec_chunked_prefill_mix),
     "long_prefill": (4, _spec_long_prefill),
     "variant_mix": (5, _spec_variant_mix),
+    "dense_prefill": (6, _spec_dense_prefill),
 }
 
 
@@ -392,6 +440,7 @@ NAMED = {
     "chunked_prefill_mix": chunked_prefill_mix,
     "long_prefill": long_prefill,
     "variant_mix": variant_mix,
+    "dense_prefill": lambda seed=6: named("dense_prefill", seed),
 }
 
 
