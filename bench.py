@@ -98,6 +98,24 @@ def _counter_per_launch(csv_path, kernel_substr, counter):
     return float(np.mean(vals)), len(vals)
 
 
+ATTENTION_KERNELS = ("ua_decode_sk_kernel", "ua_decode16_kernel", "ua_attn_lds_kernel",
+                     "ua_attn_kernel")
+
+
+def _plan_path(args):
+    """Path of the bench's plan for the workload (host-side query, no GPU)."""
+    from varlen_attention_serving_amd import binding as B
+    from varlen_attention_serving_amd import device as D
+    from varlen_attention_serving_amd import workloads as W
+    w = W.named(args.workload)
+    extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[args.force]
+    h = B.ua_create_problem(D.problem_desc(w, extra, split_segment_tiles=args.segment_tiles))
+    try:
+        return B.ua_query_plan(h, w.num_seqs, w.total_q, w.max_seqlen_q, w.max_seqlen_k).path
+    finally:
+        B.ua_destroy_problem(h)
+
+
 def summarize_traffic(args):
     """HBM bytes per launch of the attention kernel from rocprofv3 --pmc CSVs
     (FETCH_SIZE and WRITE_SIZE runs of this bench, and of --copy-calibration),
@@ -111,19 +129,23 @@ def summarize_traffic(args):
     out = {"workload": args.workload, "kernel_source_hash": kernel_source_hash(),
            "copy_calibration_bytes": copy_bytes,
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
-    for name, sub in (("attention", "ua_decode_sk_kernel" if args.force != "2d" else "ua_attn"),
-                      ("attention_2d_3d", "ua_attn_kernel"), ("reduce", "ua_reduce_kernel")):
+    for sub in ATTENTION_KERNELS + ("ua_reduce_kernel",):
         try:
             f, n = _counter_per_launch(fetch_csv, sub, "FETCH_SIZE")
             wv, _ = _counter_per_launch(write_csv, sub, "WRITE_SIZE")
         except SystemExit:
             continue
-        out["kernels"][name] = {"fetch_kib_raw": round(f, 1), "write_kib_raw": round(wv, 1),
-                                "bytes_read": round(f * 1024 * f_scale),
-                                "bytes_written": round(wv * 1024 * w_scale), "launches": n}
-    att = out["kernels"].get("attention") or out["kernels"].get("attention_2d_3d")
-    out["path"] = 3 if ("reduce" in out["kernels"]) else 2
-    out["bytes_per_launch"] = att["bytes_read"] + att["bytes_written"]
+        out["kernels"][sub] = {"fetch_kib_raw": round(f, 1), "write_kib_raw": round(wv, 1),
+                               "bytes_read": round(f * 1024 * f_scale),
+                               "bytes_written": round(wv * 1024 * w_scale), "launches": n}
+    # the dominant kernel: the attention launch that reads the most (a class
+    # split's other launch may find no rows of its class)
+    att = max((k for k in out["kernels"] if k in ATTENTION_KERNELS),
+              key=lambda k: out["kernels"][k]["bytes_read"])
+    out["attention_kernel"] = att
+    out["path"] = _plan_path(args)
+    a = out["kernels"][att]
+    out["bytes_per_launch"] = a["bytes_read"] + a["bytes_written"]
     path = os.path.join(ROOT, "profiles", f"{args.workload}_hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -177,7 +199,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
-                             "variant_mix", "tiny_varlen", "dense_prefill"])
+                             "variant_mix", "tiny_varlen", "dense_prefill", "mha_prefill"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scratch buffer between timed steps (outside the "

@@ -391,6 +391,14 @@ def _spec_dense_prefill(seed):
                         dense=True))
 
 
+def _spec_mha_prefill(seed):
+    """The transposed-V-read benchmark shape: 1 sequence S_q = S_k = 4096, MHA
+    H_q = H_k = 32, d=128, bf16, not causal, K/V packed per sequence."""
+    return dict(q_lens=[4096], seq_lens=[4096], rng=None,
+                kw=dict(num_q_heads=32, num_kv_heads=32, head_dim=128, block_size=1,
+                        causal=False, dense=True))
+
+
 NAMED_SPECS = {
     "tiny_varlen": (1, _spec_tiny_varlen),
     "decode_batch": (2, _spec_decode_batch),
@@ -398,6 +406,7 @@ NAMED_SPECS = {
     "long_prefill": (4, _spec_long_prefill),
     "variant_mix": (5, _spec_variant_mix),
     "dense_prefill": (6, _spec_dense_prefill),
+    "mha_prefill": (7, _spec_mha_prefill),
 }
 
 
@@ -441,6 +450,7 @@ NAMED = {
     "long_prefill": long_prefill,
     "variant_mix": variant_mix,
     "dense_prefill": lambda seed=6: named("dense_prefill", seed),
+    "mha_prefill": lambda seed=7: named("mha_prefill", seed),
 }
 
 
