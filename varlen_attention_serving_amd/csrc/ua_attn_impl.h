@@ -479,8 +479,47 @@ struct RowCtx {
 // QQ-bias of (row, key) in log2 units for a key of the query section; the
 // column is clamped so keys past S_k (masked) read inside the matrix
 __device__ __forceinline__ float qq_bias2(const UaKernelParams& p, const RowCtx& rc, int key) {
-    const int kl = min(key - rc.ctx, rc.qlast);
-    return p.qq_bias[(int64_t)rc.qloc * p.qq_stride + kl] * kLog2e;
+    const int kl = min(max(key - rc.ctx, 0), rc.qlast);
+    const float b = p.qq_bias[(int64_t)rc.qloc * p.qq_stride + kl] * kLog2e;
+    return key >= rc.ctx ? b : 0.0f;
+}
+
+// Scale -> softcap -> ALiBi -> QQ-bias on one lane's scores s[v][i] (key
+// key_of(v, i)), to log2 units.  Each step is one pass under one uniform
+// test of the problem's flags, so a tile pays only for the steps the problem
+// asks for and the passes stay branch-free inside.
+template <int NV, int W, typename V, typename KeyOf>
+__device__ __forceinline__ void transform_scores(const UaKernelParams& p, V (&s)[NV], KeyOf key_of,
+                                                 const RowCtx& rc, bool qq) {
+    if (p.flags & UA_FLAG_SOFTCAP) {
+        // c tanh(y) = c - 2c / (1 + e^{2y}), with e^{2y} = 2^{x * softcap_in2}:
+        // saturates to +-c for large |y| (1 / inf = 0) without a clamp
+        const float c2 = 2.0f * p.softcap_out;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                s[v][i] = p.softcap_out -
+                          c2 * __builtin_amdgcn_rcpf(1.0f + fast_exp2(s[v][i] * p.softcap_in2));
+    } else {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < W; ++i) s[v][i] *= p.qk_scale_log2;
+    }
+    if (p.flags & UA_FLAG_ALIBI) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                s[v][i] = __builtin_fmaf(rc.slope2, (float)(key_of(v, i) - rc.ctx), s[v][i]);
+    }
+    if (qq) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int i = 0; i < W; ++i) s[v][i] += qq_bias2(p, rc, key_of(v, i));
+    }
 }
 
 // Rows of one q-block: pos_local = r / g, head_local = r % g.
@@ -556,25 +595,17 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
     // Scores to log2 units.  Without softcap/ALiBi the multiplier c > 0 keeps
     // the order, so the max is taken on raw scores and the scale is folded
     // into the exponent as one FMA: 2^(x c - m).
-    const bool softcap = XFORM && (p.flags & UA_FLAG_SOFTCAP);
-    const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
     const float c = XFORM ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
-    // QQ-bias only on tiles that reach the query section (ctx is the same for
-    // every row of a q-block, so the test is uniform)
-    const bool qq = XFORM && (p.flags & UA_FLAG_QQ_BIAS) && key0 + BN > rc.ctx;
-    auto transform = [&](float x, int key) {
-        if (XFORM) {
-            // c tanh(y) = c - 2c / (1 + e^{2y}), with e^{2y} = 2^{x * softcap_in2}: saturates
-            // to +-c for large |y| (1 / inf = 0) without a clamp
-            x = softcap ? p.softcap_out - 2.0f * p.softcap_out *
-                                              __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
-                        : x * p.qk_scale_log2;
-            x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
-            if (qq && key >= rc.ctx) x += qq_bias2(p, rc, key);
-        }
-        return x;
-    };
+    if (XFORM) {
+        // QQ-bias only on tiles that reach the query section (ctx is the same
+        // for every row of a q-block, so the test is uniform)
+        const bool qq = (p.flags & UA_FLAG_QQ_BIAS) && key0 + BN > rc.ctx;
+        transform_scores<NKT, 16>(
+            p, sacc,
+            [&](int kt, int i) { return key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3); }, rc,
+            qq);
+    }
     if (need_mask) {
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
@@ -582,7 +613,7 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
             for (int i = 0; i < 16; ++i) {
                 const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
                 const bool keep = (key >= rc.kmin) & (key <= rc.kmax);
-                const float sv = keep ? transform(sacc[kt][i], key) : -INFINITY;
+                const float sv = keep ? sacc[kt][i] : -INFINITY;
                 sacc[kt][i] = sv;
                 mt = fmaxf(mt, sv);
             }
@@ -590,12 +621,7 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-                const float sv = transform(sacc[kt][i], key);
-                sacc[kt][i] = sv;
-                mt = fmaxf(mt, sv);
-            }
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
     }
     mt = fmaxf(mt, xor32(mt)) * c;
     // Lazy reference max: exponents are taken against m_run, which moves only
@@ -1381,27 +1407,19 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef Geom16<D, FP8> G;
-    const bool softcap = XFORM && (p.flags & UA_FLAG_SOFTCAP);
-    const bool alibi = XFORM && (p.flags & UA_FLAG_ALIBI);
     const float c = XFORM ? 1.0f : p.qk_scale_log2;
-    const bool qq = XFORM && (p.flags & UA_FLAG_QQ_BIAS) && key0 + G::BN > rc.ctx;
-    auto transform = [&](float x, int key) {
-        if (XFORM) {
-            x = softcap ? p.softcap_out - 2.0f * p.softcap_out *
-                                              __builtin_amdgcn_rcpf(1.0f + fast_exp2(x * p.softcap_in2))
-                        : x * p.qk_scale_log2;
-            x = alibi ? x + rc.slope2 * (float)(key - rc.ctx) : x;
-            if (qq && key >= rc.ctx) x += qq_bias2(p, rc, key);
-        }
-        return x;
-    };
+    if (XFORM) {
+        const bool qq = (p.flags & UA_FLAG_QQ_BIAS) && key0 + G::BN > rc.ctx;
+        transform_scores<2, 4>(
+            p, sacc, [&](int kb, int i) { return key0 + 16 * kb + 4 * grp + i; }, rc, qq);
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = key0 + 16 * kb + 4 * grp + i;
-            float sv = transform(sacc[kb][i], key);
+            float sv = sacc[kb][i];
             if (need_mask) sv = ((key >= rc.kmin) & (key <= rc.kmax)) ? sv : -INFINITY;
             sacc[kb][i] = sv;
             mt = fmaxf(mt, sv);
