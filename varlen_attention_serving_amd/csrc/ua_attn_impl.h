@@ -93,6 +93,13 @@ constexpr int min_waves_per_simd(int d, int waves) {
 #ifndef UA_LDS_RING
 #define UA_LDS_RING 1
 #endif
+// Score transforms a kernel is compiled for: none (the scale folds into the
+// exponent), softcap and/or ALiBi (tested per tile from the flags), or those
+// plus the QQ-bias, whose per-element loads cost registers the others need not
+// pay for.
+constexpr int kXfNone = 0;
+constexpr int kXfScore = 1;
+constexpr int kXfQQ = 2;
 // log2-unit slack before the running reference max is moved (p <= 2^8)
 constexpr float kLazyRescale = 8.0f;
 
@@ -586,7 +593,7 @@ __device__ __forceinline__ void qk_tile(const unsigned short* __restrict__ k_lds
 
 // Scores of one tile to log2 units with masks applied, and the running max
 // (O and l are re-based here when the reference max moves).
-template <int D, int BN, bool XFORM>
+template <int D, int BN, int XF>
 __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sacc)[BN / 32],
                                             f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
                                             int key0, bool need_mask, const RowCtx& rc, int half) {
@@ -595,12 +602,12 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
     // Scores to log2 units.  Without softcap/ALiBi the multiplier c > 0 keeps
     // the order, so the max is taken on raw scores and the scale is folded
     // into the exponent as one FMA: 2^(x c - m).
-    const float c = XFORM ? 1.0f : p.qk_scale_log2;
+    const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
-    if (XFORM) {
+    if (XF != 0) {
         // QQ-bias only on tiles that reach the query section (ctx is the same
         // for every row of a q-block, so the test is uniform)
-        const bool qq = (p.flags & UA_FLAG_QQ_BIAS) && key0 + BN > rc.ctx;
+        const bool qq = XF == kXfQQ && key0 + BN > rc.ctx;
         transform_scores<NKT, 16>(
             p, sacc,
             [&](int kt, int i) { return key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3); }, rc,
@@ -641,12 +648,12 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
 }
 
 // p = 2^(x c - m) in the Q type, and the running denominator.
-template <int BN, typename QT, bool XFORM>
+template <int BN, typename QT, int XF>
 __device__ __forceinline__ void softmax_exp(const UaKernelParams& p, const f32x16 (&sacc)[BN / 32],
                                             float m_run, float& l_run,
                                             typename QType<QT>::v8 (&pf)[BN / 16]) {
     typedef QType<QT> Q;
-    const float c = XFORM ? 1.0f : p.qk_scale_log2;
+    const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
     const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
@@ -686,9 +693,9 @@ __device__ __forceinline__ void pv_tile(const unsigned short* __restrict__ v_lds
 
 // One tile: scores, scale -> softcap -> ALiBi -> QQ-bias -> masks (log2 units), the
 // online-softmax update, then O^T += V^T P^T.  key0 is the tile's first key
-// position.  XFORM = false compiles the plain scale for problems without
+// position.  XF = kXfNone compiles the plain scale for problems without
 // softcap and ALiBi.
-template <int D, int BN, typename QT, bool XFORM, bool SWZ = false>
+template <int D, int BN, typename QT, int XF, bool SWZ = false>
 __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
                                             const unsigned short* __restrict__ k_lds,
                                             const unsigned short* __restrict__ v_lds,
@@ -699,8 +706,8 @@ __device__ __forceinline__ void attend_tile(const UaKernelParams& p,
     f32x16 sacc[BN / 32];
     typename QType<QT>::v8 pf[BN / 16];
     qk_tile<D, BN, QT, SWZ>(k_lds, qf, fr, sacc);
-    softmax_max<D, BN, XFORM>(p, sacc, oacc, m_run, l_run, key0, need_mask, rc, half);
-    softmax_exp<BN, QT, XFORM>(p, sacc, m_run, l_run, pf);
+    softmax_max<D, BN, XF>(p, sacc, oacc, m_run, l_run, key0, need_mask, rc, half);
+    softmax_exp<BN, QT, XF>(p, sacc, m_run, l_run, pf);
     pv_tile<D, BN, QT, SWZ>(v_lds, pf, oacc, fr);
 }
 
@@ -828,7 +835,7 @@ __device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowIn
     }
 }
 
-template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, bool XFORM>
+template <int D, int NW, int BN, typename QT, bool FP8, bool SPLIT, int XF>
 __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -897,7 +904,7 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
         if (!wave_active) continue;
         const int key0 = t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+        attend_tile<D, BN, QT, XF>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
                                fr, half);
     }
 
@@ -908,7 +915,7 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
 // The same q-block work for 16-bit K/V with four waves and block sizes of at
 // least ROWS_PER_OP keys: tiles arrive through the LDS ring instead of
 // registers (STAGES - 1 tiles in flight, one barrier per tile).
-template <int D, typename QT, bool SPLIT, bool XFORM>
+template <int D, typename QT, bool SPLIT, int XF>
 __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -999,7 +1006,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
             const unsigned short* k_lds = tiles + ST * 2 * L::TILE_ELEMS;
             const int key0 = t * BN;
             const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-            attend_tile<D, BN, QT, XFORM, true>(p, k_lds, k_lds + L::TILE_ELEMS, qf, oacc, m_run,
+            attend_tile<D, BN, QT, XF, true>(p, k_lds, k_lds + L::TILE_ELEMS, qf, oacc, m_run,
                                                 l_run, key0, need_mask, ri.rc, fr, half);
         }
     };
@@ -1155,7 +1162,7 @@ __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int
     return first;
 }
 
-template <int D, int BN, typename QT, bool FP8, bool XFORM>
+template <int D, int BN, typename QT, bool FP8, int XF>
 __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -1228,7 +1235,7 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
         }
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        attend_tile<D, BN, QT, XFORM>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
+        attend_tile<D, BN, QT, XF>(p, k_lds, v_lds, qf, oacc, m_run, l_run, key0, need_mask, ri.rc,
                                fr, half);
         if (x + 1 == B || pc.t + 1 == pc.t_end) {
             const float l_tot = l_run + xor32(l_run);
@@ -1398,7 +1405,7 @@ __device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG>& ld,
 }
 
 // transform, masks, online softmax and O^T += V^T P^T for one tile
-template <int D, typename QT, bool FP8, bool XFORM>
+template <int D, typename QT, bool FP8, int XF>
 __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sacc)[2],
                                              const unsigned short* __restrict__ v_lds,
                                              f32x4 (&oacc)[D / 16], float& m_run, float& l_run,
@@ -1407,9 +1414,9 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef Geom16<D, FP8> G;
-    const float c = XFORM ? 1.0f : p.qk_scale_log2;
-    if (XFORM) {
-        const bool qq = (p.flags & UA_FLAG_QQ_BIAS) && key0 + G::BN > rc.ctx;
+    const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
+    if (XF != 0) {
+        const bool qq = XF == kXfQQ && key0 + G::BN > rc.ctx;
         transform_scores<2, 4>(
             p, sacc, [&](int kb, int i) { return key0 + 16 * kb + 4 * grp + i; }, rc, qq);
     }
@@ -1459,7 +1466,7 @@ constexpr int min_waves16(int d, bool fp8) {
     return d <= 64 ? 4 : d <= 128 ? (fp8 ? 3 : 2) : (fp8 ? 2 : 1);
 }
 
-template <int D, typename QT, bool FP8, bool XFORM, bool BIG>
+template <int D, typename QT, bool FP8, int XF, bool BIG>
 __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -1541,7 +1548,7 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
             ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);
         }
-        softmax_pv16<D, QT, FP8, XFORM>(p, sacc, v_lds, oacc, m_run, l_run, key0, need_mask, ri.rc,
+        softmax_pv16<D, QT, FP8, XF>(p, sacc, v_lds, oacc, m_run, l_run, key0, need_mask, ri.rc,
                                         grp, v_frag);
         if (x + 1 == B || pc.t + 1 == pc.t_end) {
             float l_tot = l_run + xor16(l_run);
@@ -1731,7 +1738,7 @@ int resident_workgroups(K kernel) {
     return cache[dev];
 }
 
-template <int D, int NW, int BN, typename QT, bool FP8, bool XFORM>
+template <int D, int NW, int BN, typename QT, bool FP8, int XF>
 hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t st) {
     UaKernelParams p = p0;
     dim3 grid(l.grid[0], l.grid[1], l.grid[2]);
@@ -1745,26 +1752,26 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
                 // built for d = 256 only (the plan asks for it there)
                 if constexpr (D == 256) {
                     if (p.block_size_log2 >= 4) {
-                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM, true>),
+                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XF, true>),
                                            (int)kMaxStreamKWorkers);
                         p.sk_workers = workers;
-                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM, true>), dim3(workers),
+                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XF, true>), dim3(workers),
                                            dim3(64), 0, st, p);
                     } else {
-                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XFORM, false>),
+                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XF, false>),
                                            (int)kMaxStreamKWorkers);
                         p.sk_workers = workers;
-                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XFORM, false>), dim3(workers),
+                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XF, false>), dim3(workers),
                                            dim3(64), 0, st, p);
                     }
                 } else {
                     return hipErrorInvalidValue;
                 }
             } else {
-                workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>),
+                workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XF>),
                                    (int)kMaxStreamKWorkers);
                 p.sk_workers = workers;
-                hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XFORM>), dim3(workers), dim3(64),
+                hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XF>), dim3(workers), dim3(64),
                                    0, st, p);
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1784,15 +1791,15 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         const bool split = l.path == 3;
         if constexpr (ring_built) {
             if (ring && split)
-                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, true, XFORM>), grid, dim3(256), 0, st, p);
+                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, true, XF>), grid, dim3(256), 0, st, p);
             if (ring && !split)
-                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, false, XFORM>), grid, dim3(256), 0, st, p);
+                hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, false, XF>), grid, dim3(256), 0, st, p);
         }
         if (!ring && split)
-            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XFORM>), grid, dim3(NW * 64),
+            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XF>), grid, dim3(NW * 64),
                                0, st, p);
         if (!ring && !split)
-            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false, XFORM>), grid, dim3(NW * 64),
+            hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, false, XF>), grid, dim3(NW * 64),
                                0, st, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;
@@ -1812,27 +1819,28 @@ constexpr bool geometry_ok() {
     return (NW * 64) % cpr == 0 && BN % ((NW * 64) / cpr) == 0;
 }
 
-template <int D, int NW, int BN, typename QT, bool FP8, bool XFORM>
+template <int D, int NW, int BN, typename QT, bool FP8, int XF>
 hipError_t launch_if_built(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
-    if constexpr (geometry_ok<D, NW, BN, FP8>()) return launch_attn<D, NW, BN, QT, FP8, XFORM>(p, l, st);
+    if constexpr (geometry_ok<D, NW, BN, FP8>()) return launch_attn<D, NW, BN, QT, FP8, XF>(p, l, st);
     return hipErrorInvalidValue;
 }
 
-template <int D, typename QT, bool FP8, bool XFORM>
+template <int D, typename QT, bool FP8, int XF>
 hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
-    if (l.waves == 1 && l.tile_n == 32) return launch_if_built<D, 1, 32, QT, FP8, XFORM>(p, l, st);
-    if (l.waves == 4 && l.tile_n == 32) return launch_if_built<D, 4, 32, QT, FP8, XFORM>(p, l, st);
+    if (l.waves == 1 && l.tile_n == 32) return launch_if_built<D, 1, 32, QT, FP8, XF>(p, l, st);
+    if (l.waves == 4 && l.tile_n == 32) return launch_if_built<D, 4, 32, QT, FP8, XF>(p, l, st);
     if constexpr (D <= 128) {
-        if (l.waves == 4 && l.tile_n == 64) return launch_if_built<D, 4, 64, QT, FP8, XFORM>(p, l, st);
+        if (l.waves == 4 && l.tile_n == 64) return launch_if_built<D, 4, 64, QT, FP8, XF>(p, l, st);
     }
     return hipErrorInvalidValue;
 }
 
 template <int D, typename QT, bool FP8>
 hipError_t launch_xform(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
-    if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_QQ_BIAS))
-        return launch_geometry<D, QT, FP8, true>(p, l, st);
-    return launch_geometry<D, QT, FP8, false>(p, l, st);
+    if (p.flags & UA_FLAG_QQ_BIAS) return launch_geometry<D, QT, FP8, kXfQQ>(p, l, st);
+    if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI))
+        return launch_geometry<D, QT, FP8, kXfScore>(p, l, st);
+    return launch_geometry<D, QT, FP8, kXfNone>(p, l, st);
 }
 
 template <int D>
