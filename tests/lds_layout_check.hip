@@ -147,9 +147,12 @@ int check_v16() {
 
 // The stream-K partition: W workers split T flattened tiles into contiguous
 // ranges [jT/W, (j+1)T/W); sk_worker_of(x) must name the worker holding tile
-// x; and with random per-pair tile counts the partial slot p + j of every
-// ((sequence, kv-head) pair p, worker j) a worker touches is unique and below
-// (number of pairs) + W.  (N and G below are the pair and worker counts.)
+// x; and with random per-unit tile counts the partial slots (u + j) * H + w of
+// every (unit u, worker j) a worker touches, for each of the H waves w of a
+// worker (the kv heads of one head group), are unique and below
+// (number of units + W) * H, and the reduce's walk from the unit's first
+// worker with stride H meets exactly those slots.  (N and G below are the
+// unit and worker counts.)
 int check_stream_k() {
     int bad = 0;
     unsigned rng = 12345u;
@@ -166,19 +169,33 @@ int check_stream_k() {
         if (T == 0) continue;
         std::vector<int> first(N + 1, 0);
         for (int s = 0; s < N; ++s) first[s + 1] = first[s] + n[s];
-        std::vector<char> used((size_t)(N + G), 0);
+        const int H = 1 << (trial % 4);  // waves per worker: 1, 2, 4, 8
+        std::vector<char> used((size_t)(N + G) * H, 0);
         for (int64_t g = 0; g < G; ++g) {
             const int64_t A = g * T / G, B = (g + 1) * T / G;
             for (int64_t x = A; x < B; ++x)
                 if (sk_worker_of(x, T, G) != g) ++bad;
             if (A >= B) continue;
-            // sequences the group touches: those whose tile range meets [A, B)
+            // units the worker touches: those whose tile range meets [A, B)
             for (int s = 0; s < N; ++s) {
                 if (n[s] == 0 || first[s + 1] <= A || first[s] >= B) continue;
-                const int64_t slot = s + g;
-                if (slot >= N + G || used[slot]) ++bad;
-                used[slot] = 1;
+                for (int w = 0; w < H; ++w) {
+                    const int64_t slot = (s + g) * H + w;
+                    if (slot >= (N + G) * H || used[slot]) ++bad;
+                    used[slot] = 1;
+                }
             }
+        }
+        // the reduce reads slot ((s + g0) * H + w) + k * H for k = 0 .. g1 - g0
+        for (int s = 0; s < N; ++s) {
+            if (n[s] == 0) continue;
+            const int g0 = sk_worker_of(first[s], T, G), g1 = sk_worker_of(first[s] + n[s] - 1, T, G);
+            for (int w = 0; w < H; ++w)
+                for (int g = g0; g <= g1; ++g) {
+                    const int64_t A = (int64_t)g * T / G, B = (int64_t)(g + 1) * T / G;
+                    const int64_t slot = ((int64_t)(s + g0) * H + w) + (int64_t)(g - g0) * H;
+                    if (A < B && (slot >= (N + G) * H || !used[slot])) ++bad;
+                }
         }
         // a sequence's groups: from the group of its first tile to that of its last
         for (int s = 0; s < N; ++s) {

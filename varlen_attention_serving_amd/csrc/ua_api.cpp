@@ -459,6 +459,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.softcap_out = (d.flags & UA_FLAG_SOFTCAP) ? d.softcap * kLog2e : 0.0f;
     base.out_scale = p->fp8 ? d.v_scale : 1.0f;
     base.small_block_q = pl.small_block_q;
+    base.sk_heads = 1;
 
     // workspace: [segmented partials][stream-K partials], both 256-byte aligned
     if (a->workspace && ((uintptr_t)a->workspace & 255))

@@ -45,7 +45,10 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "ua.h"
 #include "ua_internal.h"
@@ -93,6 +96,13 @@ constexpr int min_waves_per_simd(int d, int waves) {
 #ifndef UA_LDS_RING
 #define UA_LDS_RING 1
 #endif
+// kv heads a stream-K worker workgroup serves together (a power of two; the
+// launch takes the largest that divides H_k)
+#ifndef UA_SK_HEADS
+#define UA_SK_HEADS 8
+#endif
+constexpr int kSkMaxHeads = UA_SK_HEADS;
+
 // Score transforms a kernel is compiled for: none (the scale folds into the
 // exponent), softcap and/or ALiBi (tested per tile from the flags), or those
 // plus the QQ-bias, whose per-element loads cost registers the others need not
@@ -1067,6 +1077,15 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 __device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 
+// The stream-K order flattens (sequence, kv-head group, tile).  A worker is a
+// workgroup of sk_heads waves, one per kv head of a group, that walk the same
+// tiles together, so the heads of one cached key row are fetched at the same
+// time (one contiguous run of H_k * d elements per key instead of H_k
+// separate d-element pieces at different times).
+__device__ __forceinline__ int sk_groups(const UaKernelParams& p) {
+    return p.num_kv_heads / p.sk_heads;
+}
+
 // Total tiles T and, for flattened tile x, the sequence holding it and that
 // sequence's first flattened tile.  Every lane of the wave gets the results.
 template <int BN>
@@ -1074,7 +1093,7 @@ __device__ __forceinline__ int sk_total(const UaKernelParams& p) {
     int total = 0;
     for (int base = 0; base < p.num_seqs; base += 64) {
         const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        total += readlane(wave_incl_scan(q.n * p.num_kv_heads), 63);
+        total += readlane(wave_incl_scan(q.n * sk_groups(p)), 63);
     }
     return total;
 }
@@ -1084,7 +1103,7 @@ __device__ __forceinline__ int sk_locate(const UaKernelParams& p, int64_t x, int
     int carry = 0;
     for (int base = 0; base < p.num_seqs; base += 64) {
         const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        const int v = q.n * p.num_kv_heads;
+        const int v = q.n * sk_groups(p);
         const int incl = wave_incl_scan(v);
         const uint64_t hit = __ballot((int64_t)carry + incl > x);
         if (hit) {
@@ -1129,7 +1148,7 @@ __device__ __forceinline__ SkPos sk_next(const UaKernelParams& p, const SkPos& c
         r.t = c.t + 1;
         return r;
     }
-    if (c.h + 1 < p.num_kv_heads) {
+    if (c.h + 1 < sk_groups(p)) {
         r.h = c.h + 1;
         r.t = c.t_lo;
         return r;
@@ -1149,7 +1168,7 @@ __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int
     int carry = 0, first = 0, n = 0;
     for (int base = 0; base < p.num_seqs; base += 64) {
         const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        const int v = q.n * p.num_kv_heads;
+        const int v = q.n * sk_groups(p);
         const int incl = wave_incl_scan(v);
         if (s >= base && s < base + 64) {
             first = carry + readlane(incl - v, s - base);
@@ -1162,17 +1181,27 @@ __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int
     return first;
 }
 
+// LDS of one stream-K wave (its own padded K and V tiles), in 16-bit elements
+template <int D, int BN, bool FP8>
+constexpr int sk_wave_lds_elems() {
+    return BN * (TileGeom<D, 1, BN, FP8>::KSTR + TileGeom<D, 1, BN, FP8>::VSTR);
+}
+
 template <int D, int BN, typename QT, bool FP8, int XF>
-__global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(UaKernelParams p) {
+__global__ __launch_bounds__(64 * kSkMaxHeads, min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(
+    UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef TileGeom<D, 1, BN, FP8> G;
     static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
 
-    __shared__ __attribute__((aligned(16))) unsigned short k_lds[BN * G::KSTR];
-    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * G::VSTR];
+    // sk_heads waves, each with its own tiles (dynamic LDS sized at launch)
+    extern __shared__ __attribute__((aligned(16))) unsigned short sk_lds[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned short* k_lds = sk_lds + wave * sk_wave_lds_elems<D, BN, FP8>();
+    unsigned short* v_lds = k_lds + BN * G::KSTR;
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int64_t W = gridDim.x;
     const int64_t j = blockIdx.x;
@@ -1199,7 +1228,11 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
     const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
     const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
     auto bt_row = [&](const SkPos& q) { return table_row(p, q.s); };
-    auto hoff = [&](const SkPos& q) { return q.kv_row * slot_bytes + (int64_t)q.h * D * G::ESZ; };
+    // this wave's kv head within the position's head group
+    auto head = [&](const SkPos& q) { return q.h * p.sk_heads + wave; };
+    auto hoff = [&](const SkPos& q) {
+        return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
+    };
 
     KvLoader<D, 1, BN, QT, FP8> ld;
     ld.init(lane);
@@ -1215,7 +1248,7 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
     f32x16 oacc[G::NDT];
     float m_run, l_run;
     auto begin_pair = [&](const SkPos& q) {
-        ri = row_info(p, lane & 31, q.h, q.q_start, q.q_len, q.s_k, 0);
+        ri = row_info(p, lane & 31, head(q), q.q_start, q.q_len, q.s_k, 0);
         kr = key_range(p.flags, p.window, q.s_k, q.s_k - q.q_len, 0, q.q_len - 1);
         load_q<D, QT>(p, ri, half, qf);
         m_run = -INFINITY;
@@ -1240,7 +1273,11 @@ __global__ __launch_bounds__(64, min_waves_per_simd(D, 1)) void ua_decode_sk_ker
         if (x + 1 == B || pc.t + 1 == pc.t_end) {
             const float l_tot = l_run + xor32(l_run);
             if (ri.ok) {
-                const int64_t slot = (int64_t)pc.s * p.num_kv_heads + pc.h + j;
+                // unit (sequence, head group) u and worker j give the slot
+                // (u + j) * sk_heads + wave: unique, since u and j never
+                // decrease together along the flattened order
+                const int64_t unit = (int64_t)pc.s * sk_groups(p) + pc.h;
+                const int64_t slot = (unit + j) * p.sk_heads + wave;
                 write_partial<D>(p, slot * p.rows_used + (lane & 31), half, oacc, m_run, l_tot);
             }
             if (x + 1 < B) begin_pair(p1);
@@ -1554,7 +1591,8 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
             float l_tot = l_run + xor16(l_run);
             l_tot += xor32(l_tot);
             if (ri.ok) {
-                const int64_t slot = (int64_t)pc.s * p.num_kv_heads + pc.h + j;
+                // one kv head per worker here (sk_heads = 1): slot = unit + j
+                const int64_t slot = (int64_t)pc.s * sk_groups(p) + pc.h + j;
                 const int64_t rid = slot * p.rows_used + (lane & 15);
                 float* wo = p.ws_o + rid * D + 4 * grp;
 #pragma unroll
@@ -1658,20 +1696,22 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const int64_t T = total;
         const int64_t W = p.sk_workers;
         const int hk = head2 / p.group;
-        const int64_t x0 = xs + (int64_t)hk * n;
+        const int hg = hk / p.sk_heads, wv = hk - hg * p.sk_heads;
+        const int64_t x0 = xs + (int64_t)hg * n;
         const int j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
         const int j1 = T > 0 ? sk_worker_of(x0 + n - 1, T, W) : 0;
         const int r = i * p.group + (head2 - hk * p.group);
         const int count = (n > 0 && T > 0) ? j1 - j0 + 1 : 0;
-        merge_partials<D, QT>(p, ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r,
-                              p.rows_used, count, j0, T, W, true, q_start + i, head2);
+        const int64_t slot0 = ((int64_t)s * sk_groups(p) + hg + j0) * p.sk_heads + wv;
+        merge_partials<D, QT>(p, slot0 * p.rows_used + r, (int64_t)p.sk_heads * p.rows_used, count,
+                              j0, T, W, true, q_start + i, head2);
     } else if (SK) {
         // one pass over the sequences: the token's sequence s, the first
         // flattened tile of s, its tile count and the total T
         int carry = 0, s = -1, xs = 0, n = 0, q_start = 0, q_len = 0;
         for (int base = 0; base < p.num_seqs; base += 64) {
             const SeqLane q = seq_lane<kSkTile>(p, base + lane);
-            const int v = q.n * p.num_kv_heads;
+            const int v = q.n * sk_groups(p);
             const int incl = wave_incl_scan(v);
             const bool past = base + lane < p.num_seqs && q.q_start + q.q_len <= tok;
             const uint64_t before = __ballot(!past && base + lane < p.num_seqs);
@@ -1690,13 +1730,15 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const int64_t T = carry;
         const int64_t W = p.sk_workers;
         const int hk = head / p.group;
-        const int64_t x0 = xs + (int64_t)hk * n;
+        const int hg = hk / p.sk_heads, wv = hk - hg * p.sk_heads;
+        const int64_t x0 = xs + (int64_t)hg * n;
         const int j0 = T > 0 ? sk_worker_of(x0, T, W) : 0;
         const int j1 = T > 0 ? sk_worker_of(x0 + n - 1, T, W) : 0;
         const int r = (tok - q_start) * p.group + (head - hk * p.group);
         const int count = (s >= 0 && n > 0 && T > 0) ? j1 - j0 + 1 : 0;
-        merge_partials<D, QT>(p, ((int64_t)s * p.num_kv_heads + hk + j0) * p.rows_used + r,
-                              p.rows_used, count, j0, T, W, true, tok, head);
+        const int64_t slot0 = ((int64_t)s * sk_groups(p) + hg + j0) * p.sk_heads + wv;
+        merge_partials<D, QT>(p, slot0 * p.rows_used + r, (int64_t)p.sk_heads * p.rows_used, count,
+                              j0, T, W, true, tok, head);
     } else {
         const int s = token_seq(p.cu_q, p.num_seqs, tok);
         const int q_start = p.cu_q[s];
@@ -1718,24 +1760,44 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
 // launchers
 // ---------------------------------------------------------------------------
 
-// workers of the stream-K split: as many single-wave workgroups as the device
-// holds at once (queried once per device and instantiation)
-template <typename K>
-int resident_workgroups(K kernel) {
-    static int cache[64] = {0};
+// Workers of the stream-K split: as many workgroups of `waves` waves (and
+// `lds` bytes of dynamic LDS) as the device holds at once.  Queried once per
+// (device, kernel, shape): every kernel of the family has the same function
+// type, so the kernel's address is part of the key.
+struct ResidentKey {
+    int dev;
+    const void* kernel;
+    int waves;
+    size_t lds;
+};
+
+inline int resident_workgroups_of(const void* kernel, int waves, size_t lds) {
+    static std::mutex mu;
+    static std::vector<std::pair<ResidentKey, int>> cache;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cache[dev]) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus < 1)
-            cus = 256;
-        cache[dev] = per_cu * cus;
-    }
-    return cache[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+        if (e.first.dev == dev && e.first.kernel == kernel && e.first.waves == waves &&
+            e.first.lds == lds)
+            return e.second;
+    int per_cu = 0, cus = 0;
+    if (lds > 0)
+        (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * waves, lds) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    cache.push_back({ResidentKey{dev, kernel, waves, lds}, per_cu * cus});
+    return per_cu * cus;
+}
+
+template <typename K>
+int resident_workgroups(K kernel, int waves = 1, size_t lds = 0) {
+    return resident_workgroups_of(reinterpret_cast<const void*>(kernel), waves, lds);
 }
 
 template <int D, int NW, int BN, typename QT, bool FP8, int XF>
@@ -1749,6 +1811,7 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         if constexpr (NW == 1 && BN == kSkTile) {
             int workers = 0;
             if (l.rows16) {
+                p.sk_heads = 1;  // one kv head per worker
                 // built for d = 256 only (the plan asks for it there)
                 if constexpr (D == 256) {
                     if (p.block_size_log2 >= 4) {
@@ -1768,11 +1831,15 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
                     return hipErrorInvalidValue;
                 }
             } else {
-                workers = std::min(resident_workgroups(ua_decode_sk_kernel<D, BN, QT, FP8, XF>),
-                                   (int)kMaxStreamKWorkers);
+                // workers of sk_heads waves, one kv head each
+                int gh = kSkMaxHeads;
+                while (gh > 1 && p.num_kv_heads % gh) gh >>= 1;
+                p.sk_heads = gh;
+                const size_t lds = (size_t)gh * sk_wave_lds_elems<D, BN, FP8>() * 2;
+                auto kern = ua_decode_sk_kernel<D, BN, QT, FP8, XF>;
+                workers = std::min(resident_workgroups(kern, gh, lds), (int)kMaxStreamKWorkers / gh);
                 p.sk_workers = workers;
-                hipLaunchKernelGGL((ua_decode_sk_kernel<D, BN, QT, FP8, XF>), dim3(workers), dim3(64),
-                                   0, st, p);
+                hipLaunchKernelGGL(kern, dim3(workers), dim3(64 * gh), lds, st, p);
             }
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (l.events[1] && (e = hipEventRecord(l.events[1], st)) != hipSuccess) return e;

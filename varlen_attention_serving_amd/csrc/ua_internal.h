@@ -48,6 +48,7 @@ struct UaKernelParams {
                               // small_block_q; 2: only the others
     int32_t small_block_q;    // query positions of a single-wave q-block (32 / g)
     int32_t reduce_by_seq;    // stream-K reduce rows enumerated as (seq, head, i)
+    int32_t sk_heads;         // stream-K: kv heads one worker serves together (a wave each)
 };
 
 // Upper bound on stream-K workers (sizes the workspace before the device is known).
