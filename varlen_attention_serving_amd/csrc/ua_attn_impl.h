@@ -1187,8 +1187,15 @@ constexpr int sk_wave_lds_elems() {
     return BN * (TileGeom<D, 1, BN, FP8>::KSTR + TileGeom<D, 1, BN, FP8>::VSTR);
 }
 
+// heads (waves) of one stream-K worker: as many as fit on a CU at the
+// kernel's waves per SIMD, so a worker never lowers the register budget
+template <int D>
+constexpr int sk_max_heads() {
+    return kSkMaxHeads < 4 * min_waves_per_simd(D, 1) ? kSkMaxHeads : 4 * min_waves_per_simd(D, 1);
+}
+
 template <int D, int BN, typename QT, bool FP8, int XF>
-__global__ __launch_bounds__(64 * kSkMaxHeads, min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(
+__global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) void ua_decode_sk_kernel(
     UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
@@ -1502,18 +1509,27 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
 constexpr int min_waves16(int d, bool fp8) {
     return d <= 64 ? 4 : d <= 128 ? (fp8 ? 3 : 2) : (fp8 ? 2 : 1);
 }
+// heads (waves) of one 16-row stream-K worker, as for the 32-row engine
+constexpr int sk16_max_heads(int d, bool fp8) {
+    return kSkMaxHeads < 4 * min_waves16(d, fp8) ? kSkMaxHeads : 4 * min_waves16(d, fp8);
+}
 
 template <int D, typename QT, bool FP8, int XF, bool BIG>
-__global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(UaKernelParams p) {
+__global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) void ua_decode16_kernel(
+    UaKernelParams p) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef Geom16<D, FP8> G;
     constexpr int BN = G::BN;
     static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
 
-    __shared__ __attribute__((aligned(16))) unsigned short v_lds[BN * G::VSTR];
+    // one V tile per wave (dynamic LDS sized at launch); the waves of a worker
+    // share nothing else, so they need no barrier
+    extern __shared__ __attribute__((aligned(16))) unsigned short sk16_lds[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    unsigned short* v_lds = sk16_lds + wave * (BN * G::VSTR);
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int grp = lane >> 4;
     const int64_t W = gridDim.x;
     const int64_t j = blockIdx.x;
@@ -1540,7 +1556,10 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
     const unsigned char* kc = reinterpret_cast<const unsigned char*>(p.k);
     const unsigned char* vc = reinterpret_cast<const unsigned char*>(p.v);
     auto bt_row = [&](const SkPos& q) { return table_row(p, q.s); };
-    auto hoff = [&](const SkPos& q) { return q.kv_row * slot_bytes + (int64_t)q.h * D * G::ESZ; };
+    auto head = [&](const SkPos& q) { return q.h * p.sk_heads + wave; };
+    auto hoff = [&](const SkPos& q) {
+        return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
+    };
 
     Loader16<D, QT, FP8, BIG> ld;
     ld.init(lane);
@@ -1555,7 +1574,7 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
     f32x4 oacc[G::NDB];
     float m_run, l_run;
     auto begin_pair = [&](const SkPos& q) {
-        ri = row_info(p, lane & 15, q.h, q.q_start, q.q_len, q.s_k, 0);
+        ri = row_info(p, lane & 15, head(q), q.q_start, q.q_len, q.s_k, 0);
         kr = key_range(p.flags, p.window, q.s_k, q.s_k - q.q_len, 0, q.q_len - 1);
         const QT* qp = reinterpret_cast<const QT*>(p.q) + (int64_t)ri.tok * p.q_stride_tok +
                        (int64_t)ri.head * D + 8 * grp;
@@ -1591,8 +1610,8 @@ __global__ __launch_bounds__(64, min_waves16(D, FP8)) void ua_decode16_kernel(Ua
             float l_tot = l_run + xor16(l_run);
             l_tot += xor32(l_tot);
             if (ri.ok) {
-                // one kv head per worker here (sk_heads = 1): slot = unit + j
-                const int64_t slot = (int64_t)pc.s * sk_groups(p) + pc.h + j;
+                const int64_t unit = (int64_t)pc.s * sk_groups(p) + pc.h;
+                const int64_t slot = (unit + j) * p.sk_heads + wave;
                 const int64_t rid = slot * p.rows_used + (lane & 15);
                 float* wo = p.ws_o + rid * D + 4 * grp;
 #pragma unroll
@@ -1811,28 +1830,23 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         if constexpr (NW == 1 && BN == kSkTile) {
             int workers = 0;
             if (l.rows16) {
-                p.sk_heads = 1;  // one kv head per worker
                 // built for d = 256 only (the plan asks for it there)
                 if constexpr (D == 256) {
-                    if (p.block_size_log2 >= 4) {
-                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XF, true>),
-                                           (int)kMaxStreamKWorkers);
-                        p.sk_workers = workers;
-                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XF, true>), dim3(workers),
-                                           dim3(64), 0, st, p);
-                    } else {
-                        workers = std::min(resident_workgroups(ua_decode16_kernel<D, QT, FP8, XF, false>),
-                                           (int)kMaxStreamKWorkers);
-                        p.sk_workers = workers;
-                        hipLaunchKernelGGL((ua_decode16_kernel<D, QT, FP8, XF, false>), dim3(workers),
-                                           dim3(64), 0, st, p);
-                    }
+                    int gh = sk16_max_heads(D, FP8);
+                    while (gh > 1 && p.num_kv_heads % gh) gh >>= 1;
+                    p.sk_heads = gh;
+                    const size_t lds = (size_t)gh * Geom16<D, FP8>::BN * Geom16<D, FP8>::VSTR * 2;
+                    auto kern = p.block_size_log2 >= 4 ? ua_decode16_kernel<D, QT, FP8, XF, true>
+                                                       : ua_decode16_kernel<D, QT, FP8, XF, false>;
+                    workers = std::min(resident_workgroups(kern, gh, lds), (int)kMaxStreamKWorkers / gh);
+                    p.sk_workers = workers;
+                    hipLaunchKernelGGL(kern, dim3(workers), dim3(64 * gh), lds, st, p);
                 } else {
                     return hipErrorInvalidValue;
                 }
             } else {
                 // workers of sk_heads waves, one kv head each
-                int gh = kSkMaxHeads;
+                int gh = sk_max_heads<D>();
                 while (gh > 1 && p.num_kv_heads % gh) gh >>= 1;
                 p.sk_heads = gh;
                 const size_t lds = (size_t)gh * sk_wave_lds_elems<D, BN, FP8>() * 2;
