@@ -115,6 +115,32 @@ def test_stream_k_ragged_decode(seed, hk):
     assert plan.stream_k == 1
 
 
+SK_HEAD_GROUPS = [
+    # (H_k, g, d, kv dtype): workers take the largest of 8, 4, 2, 1 kv heads
+    # dividing H_k (1 for 3, 2 for 6, 4 for 12, 8 for 16 and 32)
+    (3, 4, 128, W.DT_BF16), (6, 2, 128, W.DT_BF16), (12, 2, 64, W.DT_BF16),
+    (16, 2, 128, W.DT_FP8_E4M3), (32, 1, 64, W.DT_BF16), (6, 4, 256, W.DT_BF16),
+    (12, 2, 256, W.DT_FP8_E4M3), (4, 8, 256, W.DT_BF16),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SK_HEAD_GROUPS)))
+def test_stream_k_head_groups(i):
+    """Stream-K workers of several waves, one kv head each, over every group
+    size the launch can pick (and the single-head fallback for odd H_k), on
+    both engines, ragged lengths with empty sequences."""
+    hk, g, d, kv = SK_HEAD_GROUPS[i]
+    rng = np.random.default_rng(500 + i)
+    n = 25
+    sk = rng.integers(1, 1500, size=n, endpoint=True)
+    sk[::7] = 0
+    ql = np.minimum(sk, 1)
+    w = W.build(f"skg_{hk}_{g}_{d}", 500 + i, ql, sk, num_q_heads=g * hk, num_kv_heads=hk,
+                head_dim=d, block_size=16, kv_dtype=kv, rng=rng, use_sinks=i % 2 == 1)
+    _, plan = _full_check(w, "auto")
+    assert plan.stream_k == 1
+
+
 DECODE16 = [
     # (H_q, H_k, kv dtype, flags): d = 256 decode-shaped batches on the 16-row engine
     (4, 4, W.DT_BF16, dict()),
