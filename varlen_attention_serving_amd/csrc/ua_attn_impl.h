@@ -242,7 +242,10 @@ struct TileGeom {
 // Each thread owns one 16-byte column chunk of NCH key rows of a tile.  Block
 // ids are fetched one tile ahead of the K/V loads that use them, so a tile's
 // gather never waits on a block-table read.  Loads are branch-free: a key past
-// S_k reads the sequence's last valid slot and is replaced by zeros.
+// S_k reads the sequence's last valid slot (finite data; its score is masked,
+// so its p is exactly 0).  The loaded words go to their registers untouched:
+// any use at load time (a select, say) would make each load wait for its data
+// and serialise the tile's gather.
 template <int D, int NW, int BN, typename QT, bool FP8>
 struct KvLoader {
     typedef TileGeom<D, NW, BN, FP8> G;
@@ -271,12 +274,8 @@ struct KvLoader {
             const int key = t * BN + row0 + i * G::RSTEP;
             const int kc = min(key, s_k - 1);
             const int64_t off = (((int64_t)phys[i] << lb) + (kc & bmask)) * slot_bytes + col;
-            u32x4 kw = *reinterpret_cast<const u32x4*>(base_k + off);
-            u32x4 vw = *reinterpret_cast<const u32x4*>(base_v + off);
-            const bool ok = key < s_k;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[i] = ok ? kw : z;
-            vreg[i] = ok ? vw : z;
+            kreg[i] = *reinterpret_cast<const u32x4*>(base_k + off);
+            vreg[i] = *reinterpret_cast<const u32x4*>(base_v + off);
         }
     }
     __device__ __forceinline__ void store(unsigned short* k_lds, unsigned short* v_lds) const {
@@ -761,7 +760,8 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 
 // The one block id of the dense K/V layout: a whole sequence is one block
 // (block_size_log2 = 30) whose rows start at the sequence's row offset.
-__constant__ int32_t kDenseBlockId[1] = {0};
+// (global memory, like the block table, so the table read stays a global load)
+__device__ int32_t kDenseBlockId[1] = {0};
 
 // S_k of sequence s.  Paged: clamped to the block table's width, since a
 // longer length would read past the table (a violated precondition).  Dense:
@@ -1226,9 +1226,14 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         pc.h = off / n;
         pc.t = pc.t_lo + (off - pc.h * n);
     }
-    SkPos p1 = pc, p2 = pc;
+    // fp8 tiles carry half the bytes of 16-bit ones, so fp8 workers keep two
+    // tiles in flight (two register buffers, used alternately) to hold as
+    // many bytes in flight; 16-bit workers keep one
+    constexpr int NB = (FP8 && D <= 128) ? 2 : 1;
+    SkPos p1 = pc, p2 = pc, p3 = pc;
     if (A + 1 < B) p1 = sk_next<BN>(p, pc);
     if (A + 2 < B) p2 = sk_next<BN>(p, p1);
+    if (NB == 2 && A + 3 < B) p3 = sk_next<BN>(p, p2);
 
     const int lb = p.block_size_log2;
     const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
@@ -1241,12 +1246,23 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
     };
 
-    KvLoader<D, 1, BN, QT, FP8> ld;
-    ld.init(lane);
+    KvLoader<D, 1, BN, QT, FP8> ldA, ldB;
+    ldA.init(lane);
+    ldB.init(lane);
     const Frag fr = padded_frag<D>(lane);
-    ld.ids(bt_row(pc), pc.t, pc.s_k, lb);
-    ld.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
-    if (A + 1 < B) ld.ids(bt_row(p1), p1.t, p1.s_k, lb);
+    ldA.ids(bt_row(pc), pc.t, pc.s_k, lb);
+    ldA.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
+    if (NB == 1) {
+        if (A + 1 < B) ldA.ids(bt_row(p1), p1.t, p1.s_k, lb);
+    } else {
+        // tile A + 1 into the second buffer; ids of tile A + 2 into the first
+        // (its load has been issued, so its ids are free)
+        if (A + 1 < B) {
+            ldB.ids(bt_row(p1), p1.t, p1.s_k, lb);
+            ldB.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
+        }
+        if (A + 2 < B) ldA.ids(bt_row(p2), p2.t, p2.s_k, lb);
+    }
 
     // state of the pair being accumulated
     RowInfo ri;
@@ -1265,13 +1281,21 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
     };
     begin_pair(pc);
 
-    for (int64_t x = A; x < B; ++x) {
+    // Tile x sits in buffer X; NB = 1: refill X with tile x + 1 and fetch the
+    // ids of x + 2; NB = 2: refill X with tile x + 2 and fetch the ids of
+    // x + 3 into the other buffer Y (whose load of x + 1 is in flight).
+    auto step = [&](auto& ldX, auto& ldY, int64_t x) {
         __syncthreads();
-        ld.store(k_lds, v_lds);
+        ldX.store(k_lds, v_lds);
         __syncthreads();
-        if (x + 1 < B) {
-            ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
-            if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb);
+        if (NB == 1) {
+            if (x + 1 < B) {
+                ldX.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
+                if (x + 2 < B) ldX.ids(bt_row(p2), p2.t, p2.s_k, lb);
+            }
+        } else {
+            if (x + 2 < B) ldX.load(kc + hoff(p2), vc + hoff(p2), p2.t, p2.s_k, lb, slot_bytes);
+            if (x + 3 < B) ldY.ids(bt_row(p3), p3.t, p3.s_k, lb);
         }
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
@@ -1291,7 +1315,21 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         }
         pc = p1;
         p1 = p2;
-        if (x + 3 < B) p2 = sk_next<BN>(p, p2);
+        if (NB == 1) {
+            if (x + 3 < B) p2 = sk_next<BN>(p, p2);
+        } else {
+            p2 = p3;
+            if (x + 4 < B) p3 = sk_next<BN>(p, p3);
+        }
+    };
+    if (NB == 1) {
+        for (int64_t x = A; x < B; ++x) step(ldA, ldA, x);
+    } else {
+        // unrolled by the two buffers so each keeps its own registers
+        for (int64_t x = A; x < B; x += 2) {
+            step(ldA, ldB, x);
+            if (x + 1 < B) step(ldB, ldA, x + 1);
+        }
     }
 }
 
@@ -1389,9 +1427,7 @@ struct Loader16 {
             const int ph = BIG ? ((vrow0 + i * G::RSTEP) >= 16 ? kphys[1] : kphys[0])
                                : vphys[BIG ? 0 : i];
             const int64_t off = (((int64_t)ph << lb) + (kc2 & bmask)) * slot_bytes + col;
-            const u32x4 w = *reinterpret_cast<const u32x4*>(base_v + off);
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            vreg[i] = key < s_k ? w : z;
+            vreg[i] = *reinterpret_cast<const u32x4*>(base_v + off);  // untouched until stored
         }
     }
     // the K operand of (kb, kc) in the Q type
