@@ -1226,14 +1226,9 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         pc.h = off / n;
         pc.t = pc.t_lo + (off - pc.h * n);
     }
-    // fp8 tiles carry half the bytes of 16-bit ones, so fp8 workers keep two
-    // tiles in flight (two register buffers, used alternately) to hold as
-    // many bytes in flight; 16-bit workers keep one
-    constexpr int NB = (FP8 && D <= 128) ? 2 : 1;
-    SkPos p1 = pc, p2 = pc, p3 = pc;
+    SkPos p1 = pc, p2 = pc;
     if (A + 1 < B) p1 = sk_next<BN>(p, pc);
     if (A + 2 < B) p2 = sk_next<BN>(p, p1);
-    if (NB == 2 && A + 3 < B) p3 = sk_next<BN>(p, p2);
 
     const int lb = p.block_size_log2;
     const int64_t slot_bytes = p.kv_slot_stride * G::ESZ;
@@ -1246,23 +1241,12 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
     };
 
-    KvLoader<D, 1, BN, QT, FP8> ldA, ldB;
-    ldA.init(lane);
-    ldB.init(lane);
+    KvLoader<D, 1, BN, QT, FP8> ld;
+    ld.init(lane);
     const Frag fr = padded_frag<D>(lane);
-    ldA.ids(bt_row(pc), pc.t, pc.s_k, lb);
-    ldA.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
-    if (NB == 1) {
-        if (A + 1 < B) ldA.ids(bt_row(p1), p1.t, p1.s_k, lb);
-    } else {
-        // tile A + 1 into the second buffer; ids of tile A + 2 into the first
-        // (its load has been issued, so its ids are free)
-        if (A + 1 < B) {
-            ldB.ids(bt_row(p1), p1.t, p1.s_k, lb);
-            ldB.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
-        }
-        if (A + 2 < B) ldA.ids(bt_row(p2), p2.t, p2.s_k, lb);
-    }
+    ld.ids(bt_row(pc), pc.t, pc.s_k, lb);
+    ld.load(kc + hoff(pc), vc + hoff(pc), pc.t, pc.s_k, lb, slot_bytes);
+    if (A + 1 < B) ld.ids(bt_row(p1), p1.t, p1.s_k, lb);
 
     // state of the pair being accumulated
     RowInfo ri;
@@ -1281,21 +1265,13 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
     };
     begin_pair(pc);
 
-    // Tile x sits in buffer X; NB = 1: refill X with tile x + 1 and fetch the
-    // ids of x + 2; NB = 2: refill X with tile x + 2 and fetch the ids of
-    // x + 3 into the other buffer Y (whose load of x + 1 is in flight).
-    auto step = [&](auto& ldX, auto& ldY, int64_t x) {
+    for (int64_t x = A; x < B; ++x) {
         __syncthreads();
-        ldX.store(k_lds, v_lds);
+        ld.store(k_lds, v_lds);
         __syncthreads();
-        if (NB == 1) {
-            if (x + 1 < B) {
-                ldX.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
-                if (x + 2 < B) ldX.ids(bt_row(p2), p2.t, p2.s_k, lb);
-            }
-        } else {
-            if (x + 2 < B) ldX.load(kc + hoff(p2), vc + hoff(p2), p2.t, p2.s_k, lb, slot_bytes);
-            if (x + 3 < B) ldY.ids(bt_row(p3), p3.t, p3.s_k, lb);
+        if (x + 1 < B) {
+            ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
+            if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb);
         }
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
@@ -1315,21 +1291,7 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         }
         pc = p1;
         p1 = p2;
-        if (NB == 1) {
-            if (x + 3 < B) p2 = sk_next<BN>(p, p2);
-        } else {
-            p2 = p3;
-            if (x + 4 < B) p3 = sk_next<BN>(p, p3);
-        }
-    };
-    if (NB == 1) {
-        for (int64_t x = A; x < B; ++x) step(ldA, ldA, x);
-    } else {
-        // unrolled by the two buffers so each keeps its own registers
-        for (int64_t x = A; x < B; x += 2) {
-            step(ldA, ldB, x);
-            if (x + 1 < B) step(ldB, ldA, x + 1);
-        }
+        if (x + 3 < B) p2 = sk_next<BN>(p, p2);
     }
 }
 
