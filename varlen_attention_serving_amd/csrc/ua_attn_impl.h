@@ -900,14 +900,28 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
     ld.init(tid);
     const Frag fr = padded_frag<D>(lane);
 
+    // The next tile's loads are issued before this tile's compute, except for
+    // four-wave workgroups at d = 256: there the O and Q registers leave no
+    // room to hold a tile in flight, and the spills it forced (each reload
+    // waiting for every load in flight) cost more than the overlap gave
+    // (measured: d = 256 prefill 482 -> 618 TFLOP/s without it).  Those
+    // workgroups load each tile after the barrier and rely on the other
+    // workgroup on the CU to cover the latency.
+    constexpr bool PF = !(D == 256 && NW == 4);
     ld.ids(bt, t_lo, s_k, lb);
-    ld.load(base_k, base_v, t_lo, s_k, lb, slot_bytes);
-    if (t_lo + 1 < t_hi) ld.ids(bt, t_lo + 1, s_k, lb);
+    if (PF) {
+        ld.load(base_k, base_v, t_lo, s_k, lb, slot_bytes);
+        if (t_lo + 1 < t_hi) ld.ids(bt, t_lo + 1, s_k, lb);
+    }
     for (int t = t_lo; t < t_hi; ++t) {
+        if (!PF) {
+            ld.load(base_k, base_v, t, s_k, lb, slot_bytes);
+            if (t + 1 < t_hi) ld.ids(bt, t + 1, s_k, lb);
+        }
         __syncthreads();  // every wave is done with the previous tile
         ld.store(k_lds, v_lds);
         __syncthreads();
-        if (t + 1 < t_hi) {
+        if (PF && t + 1 < t_hi) {
             ld.load(base_k, base_v, t + 1, s_k, lb, slot_bytes);  // in flight during compute
             if (t + 2 < t_hi) ld.ids(bt, t + 2, s_k, lb);
         }
