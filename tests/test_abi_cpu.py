@@ -217,13 +217,14 @@ def _named_plan(name, extra=0, split_segment_tiles=0):
 
 @pytest.mark.parametrize("name,path,split", [("tiny_varlen", 2, 0), ("decode_batch", 3, 0),
                                              ("chunked_prefill_mix", 2, 0),
-                                             ("long_prefill", 2, 0), ("variant_mix", 3, 1)])
+                                             ("long_prefill", 2, 0), ("variant_mix", 2, 1)])
 def test_shape_rule(name, path, split):
     """2D when the q-block x kv-head grid fills the device or a q-block visits
     few keys (short context or a short window); otherwise the split path.
     Wide batches on the register-staged path (fp8 K/V, d = 256) send their
-    decode-shaped sequences to a stream-K launch; on the LDS ring a batch
-    whose full grid fills one resident round stays one 2D launch."""
+    decode-shaped sequences to a stream-K launch and keep the rest as one
+    unsegmented 2D launch beside it; on the LDS ring a batch whose full grid
+    fills one resident round stays one 2D launch."""
     plan, ws = _named_plan(name)
     assert plan.path == path
     assert plan.class_split == split
@@ -233,9 +234,6 @@ def test_shape_rule(name, path, split):
         assert plan.waves == 4 and plan.stream_k == 1
     if path == 2:
         assert plan.num_segments == 1 and plan.grid[2] == 1
-    if name == "variant_mix":
-        # the window bounds the keys a q-block visits: segments cover that span
-        assert plan.num_segments >= 2 and plan.tiles_per_segment >= 4
     assert ws < (3 << 30)
 
 
