@@ -354,6 +354,60 @@ def test_block_table_permutation_is_bitwise_invariant():
         assert np.array_equal(base, moved)
 
 
+BIG_POOL_CASES = [
+    # (name, H_q, H_k, d, kv dtype, q lengths): blocks placed past 2^31 bytes
+    ("ring_prefill", 8, 8, 128, W.DT_BF16, (40, 70, 1, 3)),
+    ("stream_k_decode", 32, 8, 128, W.DT_BF16, (1, 1, 1, 1, 1)),
+    ("registers_fp8", 8, 8, 128, W.DT_FP8_E4M3, (40, 70, 1, 3)),
+    ("decode16_d256", 16, 4, 256, W.DT_BF16, (1, 1, 2)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BIG_POOL_CASES)))
+def test_blocks_beyond_2gib_of_pool(i):
+    """[UA] section 7.2: pools above 2^31 bytes need 64-bit addresses.  The
+    batch's blocks are moved to physical ids whose byte offsets lie past
+    2^31 (and past 2^32 for the last ones) in a pool of that size; the output
+    must equal the compact pool's bit for bit."""
+    name, hq, hk, d, kv, ql = BIG_POOL_CASES[i]
+    rng = np.random.default_rng(600 + i)
+    ql = np.asarray(ql)
+    sk = ql + rng.integers(0, 400, size=ql.size)
+    w = W.build(f"big_{name}", 600 + i, ql, sk, num_q_heads=hq, num_kv_heads=hk, head_dim=d,
+                block_size=16, kv_dtype=kv, rng=rng)
+    small, plan = run_hip(w)
+    compare(small, oracle.attention(w), f"big pool/{name} (compact)")
+    esz = 1 if kv == W.DT_FP8_E4M3 else 2
+    block_bytes = 16 * hk * d * esz
+    first = (1 << 31) // block_bytes + 7           # the first moved block starts past 2^31
+    spread = (1 << 32) // block_bytes - first + 64  # and the ids reach past 2^32
+    used = np.unique(w.block_table[w.block_table >= 0])
+    new_id = np.full(w.num_blocks, -1, dtype=np.int64)
+    new_id[used] = first + np.sort(rng.choice(spread, size=used.size, replace=False))
+    pool = int(new_id.max()) + 1
+    say(f"[gpu] big pool/{name}: {pool} blocks of {block_bytes} B "
+        f"({pool * block_bytes / 2**30:.2f} GiB per cache)")
+    batch = D.DeviceBatch(w)
+    big_k = torch.empty((pool,) + tuple(batch.k.shape[1:]), dtype=batch.k.dtype, device="cuda")
+    big_v = torch.empty_like(big_k)
+    idx = torch.from_numpy(new_id[used]).cuda()
+    src = torch.from_numpy(used.astype(np.int64)).cuda()
+    big_k[idx] = batch.k[src]
+    big_v[idx] = batch.v[src]
+    table = np.where(w.block_table >= 0, new_id[np.maximum(w.block_table, 0)], -1)
+    batch.k, batch.v = big_k, big_v
+    batch.block_table = torch.from_numpy(table.astype(np.int32)).cuda()
+    desc = D.problem_desc(w)
+    desc.num_blocks = pool
+    ua = D.UnifiedAttention(desc)
+    info = ua.plan(w)
+    assert info.use_i64_kv == 1 and (info.path, info.stream_k) == (plan.path, plan.stream_k)
+    moved, _ = run_hip(w, batch=batch, ua=ua)
+    assert np.array_equal(moved, small)
+    del big_k, big_v, batch
+    torch.cuda.empty_cache()
+
+
 def test_run_to_run_determinism():
     w = W.random_small(45, num_seqs=4, max_q=60, max_k=500, num_q_heads=16, num_kv_heads=4,
                        head_dim=128, block_size=32, use_sinks=True)
