@@ -761,7 +761,7 @@ __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t r
 // The one block id of the dense K/V layout: a whole sequence is one block
 // (block_size_log2 = 30) whose rows start at the sequence's row offset.
 // (global memory, like the block table, so the table read stays a global load)
-__device__ int32_t kDenseBlockId[1] = {0};
+static __device__ int32_t kDenseBlockId[1] = {0};
 
 // S_k of sequence s.  Paged: clamped to the block table's width, since a
 // longer length would read past the table (a violated precondition).  Dense:
@@ -1102,12 +1102,29 @@ __device__ __forceinline__ int sk_groups(const UaKernelParams& p) {
 
 // Total tiles T and, for flattened tile x, the sequence holding it and that
 // sequence's first flattened tile.  Every lane of the wave gets the results.
+// The scans below take sequences 256 at a time: the facts of four 64-lane
+// chunks are loaded together (one round of loads instead of four), then
+// scanned chunk by chunk.
+constexpr int kSkScanChunks = 4;
+
+// tile counts of sequences base + 64 c + lane, c < kSkScanChunks
+template <int BN>
+__device__ __forceinline__ void sk_counts(const UaKernelParams& p, int base,
+                                          int (&n)[kSkScanChunks]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < kSkScanChunks; ++c) n[c] = seq_lane<BN>(p, base + 64 * c + lane).n;
+}
+
 template <int BN>
 __device__ __forceinline__ int sk_total(const UaKernelParams& p) {
     int total = 0;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        total += readlane(wave_incl_scan(q.n * sk_groups(p)), 63);
+    for (int base = 0; base < p.num_seqs; base += 64 * kSkScanChunks) {
+        int n[kSkScanChunks];
+        sk_counts<BN>(p, base, n);
+#pragma unroll
+        for (int c = 0; c < kSkScanChunks; ++c)
+            total += readlane(wave_incl_scan(n[c] * sk_groups(p)), 63);
     }
     return total;
 }
@@ -1115,17 +1132,21 @@ __device__ __forceinline__ int sk_total(const UaKernelParams& p) {
 template <int BN>
 __device__ __forceinline__ int sk_locate(const UaKernelParams& p, int64_t x, int* seq_first) {
     int carry = 0;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        const int v = q.n * sk_groups(p);
-        const int incl = wave_incl_scan(v);
-        const uint64_t hit = __ballot((int64_t)carry + incl > x);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            *seq_first = carry + readlane(incl - v, l);
-            return base + l;
+    for (int base = 0; base < p.num_seqs; base += 64 * kSkScanChunks) {
+        int n[kSkScanChunks];
+        sk_counts<BN>(p, base, n);
+#pragma unroll
+        for (int c = 0; c < kSkScanChunks; ++c) {
+            const int v = n[c] * sk_groups(p);
+            const int incl = wave_incl_scan(v);
+            const uint64_t hit = __ballot((int64_t)carry + incl > x);
+            if (hit) {
+                const int l = __builtin_ctzll(hit);
+                *seq_first = carry + readlane(incl - v, l);
+                return base + 64 * c + l;
+            }
+            carry += readlane(incl, 63);
         }
-        carry += readlane(incl, 63);
     }
     *seq_first = carry;
     return p.num_seqs;
@@ -1180,15 +1201,20 @@ __device__ __forceinline__ SkPos sk_next(const UaKernelParams& p, const SkPos& c
 template <int BN>
 __device__ __forceinline__ int sk_seq_prefix(const UaKernelParams& p, int s, int* n_s, int* total) {
     int carry = 0, first = 0, n = 0;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-        const SeqLane q = seq_lane<BN>(p, base + (threadIdx.x & 63));
-        const int v = q.n * sk_groups(p);
-        const int incl = wave_incl_scan(v);
-        if (s >= base && s < base + 64) {
-            first = carry + readlane(incl - v, s - base);
-            n = readlane(q.n, s - base);
+    for (int base = 0; base < p.num_seqs; base += 64 * kSkScanChunks) {
+        int nc[kSkScanChunks];
+        sk_counts<BN>(p, base, nc);
+#pragma unroll
+        for (int c = 0; c < kSkScanChunks; ++c) {
+            const int b = base + 64 * c;
+            const int v = nc[c] * sk_groups(p);
+            const int incl = wave_incl_scan(v);
+            if (s >= b && s < b + 64) {
+                first = carry + readlane(incl - v, s - b);
+                n = readlane(nc[c], s - b);
+            }
+            carry += readlane(incl, 63);
         }
-        carry += readlane(incl, 63);
     }
     *n_s = n;
     *total = carry;
@@ -1740,21 +1766,28 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         // one pass over the sequences: the token's sequence s, the first
         // flattened tile of s, its tile count and the total T
         int carry = 0, s = -1, xs = 0, n = 0, q_start = 0, q_len = 0;
-        for (int base = 0; base < p.num_seqs; base += 64) {
-            const SeqLane q = seq_lane<kSkTile>(p, base + lane);
-            const int v = q.n * sk_groups(p);
-            const int incl = wave_incl_scan(v);
-            const bool past = base + lane < p.num_seqs && q.q_start + q.q_len <= tok;
-            const uint64_t before = __ballot(!past && base + lane < p.num_seqs);
-            if (s < 0 && before) {
-                const int l = __builtin_ctzll(before);
-                s = base + l;
-                xs = carry + readlane(incl - v, l);
-                n = readlane(q.n, l);
-                q_start = readlane(q.q_start, l);
-                q_len = readlane(q.q_len, l);
+        for (int base = 0; base < p.num_seqs; base += 64 * kSkScanChunks) {
+            SeqLane qc[kSkScanChunks];
+#pragma unroll
+            for (int c = 0; c < kSkScanChunks; ++c) qc[c] = seq_lane<kSkTile>(p, base + 64 * c + lane);
+#pragma unroll
+            for (int c = 0; c < kSkScanChunks; ++c) {
+                const SeqLane& q = qc[c];
+                const int b = base + 64 * c;
+                const int v = q.n * sk_groups(p);
+                const int incl = wave_incl_scan(v);
+                const bool past = b + lane < p.num_seqs && q.q_start + q.q_len <= tok;
+                const uint64_t before = __ballot(!past && b + lane < p.num_seqs);
+                if (s < 0 && before) {
+                    const int l = __builtin_ctzll(before);
+                    s = b + l;
+                    xs = carry + readlane(incl - v, l);
+                    n = readlane(q.n, l);
+                    q_start = readlane(q.q_start, l);
+                    q_len = readlane(q.q_len, l);
+                }
+                carry += readlane(incl, 63);
             }
-            carry += readlane(incl, 63);
         }
         // rows of the wide launch's sequences are that launch's to write
         if (p.class_mode == 1 && q_len > p.small_block_q) return;
