@@ -29,12 +29,19 @@
 // Paged gather.  Key position k of sequence s lives in physical block
 // block_table[s][k >> log2 b], slot k & (b - 1); its row for KV head h_k is
 // D contiguous elements at ((phys * b + slot) * H_k + h_k) * D, computed in
-// 64-bit so pools above 2^31 bytes address correctly (section 7.2).  Each KV
-// tile is copied global -> registers -> LDS (rows padded by 8 elements for K
-// and 32 for V, which spreads the K fragment reads and the transposing V
-// reads over all 64 banks).  Keys at or past S_k are written as zeros and
-// masked, so poisoned tail slots and unused blocks never reach O.  The next
-// tile's global loads are issued before the current tile is computed.
+// 64-bit so pools above 2^31 bytes address correctly (section 7.2).  The dense
+// layout of section 8 is the same with one block of 2^30 rows per sequence,
+// based at its cu_seqlens_k row.  Tiles of 16-bit K/V in four-wave workgroups
+// (d <= 128) are copied global -> LDS directly into a three-stage ring with
+// 16-byte chunks permuted against bank conflicts; every other tile goes global
+// -> registers -> LDS rows padded by 8 (K) and 32 (V) elements, which spread the
+// K fragment reads and the transposing V reads over all 64 banks.  Keys at or
+// past S_k read slot S_k - 1 (finite data) and are masked, so poisoned tail
+// slots and unused blocks never reach O.
+//
+// Decode-shaped batches run as stream-K workers over the flattened (sequence,
+// kv-head group, tile) space with a log-sum-exp reduce; at d = 256 their
+// q-blocks are 16 rows on the 16x16x32 MFMA.
 //
 // fp8 e4m3 K/V (section 7.3) are converted to the Q type on the way into LDS
 // (exact); k_scale is folded into the score multiplier and v_scale into the
@@ -1405,8 +1412,8 @@ struct Loader16 {
             }
         }
     }
-    // K straight into operand registers (keys past S_k read slot S_k - 1 and
-    // are masked); V rows as 16-byte chunks, keys past S_k zeroed
+    // K straight into operand registers, V rows as 16-byte chunks; keys past
+    // S_k read slot S_k - 1 and are masked (p = 0)
     __device__ __forceinline__ void load(const unsigned char* base_k, const unsigned char* base_v,
                                          int t, int s_k, int lb, int64_t slot_bytes, int lane) {
         const int bmask = (1 << lb) - 1;
