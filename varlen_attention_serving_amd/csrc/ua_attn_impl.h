@@ -596,13 +596,27 @@ __device__ __forceinline__ void qk_tile(const unsigned short* __restrict__ k_lds
     constexpr int KSTR = D + kKPad;
 #pragma unroll
     for (int kt = 0; kt < BN / 32; ++kt) {
-        sacc[kt] = f32x16{};
+        v8 a[D / 16];
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
             const int off = SWZ ? fr.k + kt * 32 * D + 8 * ((2 * kc) ^ fr.kx)
                                 : fr.k + kt * 32 * KSTR + 16 * kc;
-            v8 a = *reinterpret_cast<const v8*>(&k_lds[off]);
-            sacc[kt] = Q::mma(a, qf[kc], sacc[kt]);
+            a[kc] = *reinterpret_cast<const v8*>(&k_lds[off]);
+        }
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) sacc[kt] = Q::mma(a[kc], qf[kc], sacc[kt]);
+        if constexpr (SWZ) {
+            // On the ring, keep four fragment reads ahead of the MFMA chain
+            // (then one read per MFMA): the default schedule kept two, and
+            // each MFMA waited on its read (measured about +0.6-3% on prefill).
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+#pragma unroll
+            for (int i = 0; i < D / 16 - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     }
 }
