@@ -60,6 +60,10 @@ SMALL_CASES = [
     ("alibi", dict(use_alibi=True)),
     ("window", dict(window=37)),
     ("window_noncausal", dict(window=29, causal=False)),
+    # the narrowest window: a causal row sees its own key only; a non-causal
+    # row sees its own key and every later one
+    ("window1", dict(window=1)),
+    ("window1_noncausal_sinks", dict(window=1, causal=False, use_sinks=True)),
     ("sinks", dict(use_sinks=True)),
     ("all_flags", dict(softcap=5.0, use_alibi=True, window=45, use_sinks=True)),
     ("f16", dict(q_dtype=W.DT_F16, kv_dtype=W.DT_F16)),
@@ -208,6 +212,42 @@ def test_small_block_sizes(d, b):
                        num_kv_heads=2, head_dim=d, block_size=b, use_sinks=True)
     for force in ("2d", "3d"):
         _full_check(w, force, f"b={b}/d={d}/{force}")
+
+
+@pytest.mark.parametrize("d,b,kv", [(64, 1024, W.DT_BF16), (128, 256, W.DT_BF16),
+                                     (128, 512, W.DT_FP8_E4M3), (256, 128, W.DT_FP8_E4M3)])
+def test_large_block_sizes(d, b, kv):
+    """Blocks up to the largest size the descriptor accepts (1024 keys): a
+    sequence spans one or two blocks and a tile lies inside one block."""
+    w = W.random_small(540 + d + b, num_seqs=5, max_q=80, max_k=1500, num_q_heads=8,
+                       num_kv_heads=2, head_dim=d, block_size=b, kv_dtype=kv, use_sinks=True)
+    for force in ("2d", "3d"):
+        _full_check(w, force, f"b={b}/d={d}/{force}")
+
+
+MANY_SEQS = [
+    # (sequences, H_k, d, kv dtype, force)
+    (700, 2, 128, W.DT_BF16, "3d"),
+    (700, 2, 128, W.DT_BF16, "2d"),
+    (1500, 1, 64, W.DT_BF16, "3d"),
+    (600, 2, 256, W.DT_FP8_E4M3, "3d"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MANY_SEQS)))
+def test_many_sequences(i):
+    """Batches of hundreds to thousands of short sequences (some empty, some of
+    two rows): the stream-K workers' and the reduce's sequence scans take
+    several rounds of 256 sequences, and the 2D grid maps many q-blocks."""
+    n, hk, d, kv, force = MANY_SEQS[i]
+    rng = np.random.default_rng(700 + i)
+    sk = rng.integers(0, 300, size=n, endpoint=True)
+    ql = np.minimum(sk, rng.integers(0, 2, size=n, endpoint=True))
+    w = W.build(f"many_{n}_{d}", 700 + i, ql, sk, num_q_heads=4 * hk, num_kv_heads=hk,
+                head_dim=d, block_size=16, kv_dtype=kv, rng=rng, use_sinks=i % 2 == 0)
+    _, plan = _full_check(w, force, f"n={n}/d={d}/{force}")
+    if force == "3d":
+        assert plan.stream_k == 1
 
 
 QQ_CASES = [
