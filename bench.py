@@ -199,7 +199,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
-                             "variant_mix", "tiny_varlen", "dense_prefill", "mha_prefill"])
+                             "variant_mix", "tiny_varlen", "dense_prefill", "mha_prefill",
+                             "d256_prefill"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scratch buffer between timed steps (outside the "

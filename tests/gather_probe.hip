@@ -84,11 +84,8 @@ __global__ __launch_bounds__(NW * 64) void probe_registers(ProbeArgs a) {
 template <int D>
 hipError_t launch(int path, int waves, int fp8_to, const ProbeArgs& a, int n, hipStream_t st) {
     if (path == 0) {
-        if constexpr (D <= 128) {
-            hipLaunchKernelGGL(probe_ring<D>, dim3(n), dim3(256), 0, st, a);
-            return hipGetLastError();
-        }
-        return hipErrorInvalidValue;
+        hipLaunchKernelGGL(probe_ring<D>, dim3(n), dim3(256), 0, st, a);
+        return hipGetLastError();
     }
     // fp8_to: 0 = 16-bit cache, 1 = e4m3 -> bf16, 2 = e4m3 -> f16
     if (waves == 1 && fp8_to == 0) hipLaunchKernelGGL((probe_registers<D, 1, __bf16, false>), dim3(n), dim3(64), 0, st, a);
@@ -108,7 +105,7 @@ hipError_t launch(int path, int waves, int fp8_to, const ProbeArgs& a, int n, hi
 
 }  // namespace
 
-// path 0 = LDS ring (16-bit, d <= 128, block size >= 1024 / (2 d)); path 1 =
+// path 0 = LDS ring (16-bit, block size >= 1024 / (2 d)); path 1 =
 // register-staged gather with `waves` waves.  Returns 0 on success.
 extern "C" int uap_gather(int path, int waves, int fp8_to, int head_dim, const void* k, const void* v,
                           const int32_t* block_table, const int32_t* seq_lens, int bt_stride,

@@ -39,15 +39,15 @@ int check_layout() {
                 const int first = (w + 4 * g) * L::ROWS_PER_OP;
                 for (int v = 0; v < 2; ++v) {
                     const int byte = (w + 4 * g) * 1024 + v * img + 16 * lane;
-                    const int off = v ? cp.voff[g] : cp.koff[g];
-                    const unsigned rel = v ? cp.vrel[g] : cp.krel[g];
+                    const int off = v ? cp.voff(g) : cp.koff(g);
+                    const unsigned rel = v ? cp.vrel(g) : cp.krel(g);
                     if (byte < 0 || byte + 16 > 2 * img) { ++bad; continue; }
-                    if (cp.row[g] < 0 || cp.row[g] >= L::BN || off < 0 || off + 16 > L::RB) ++bad;
-                    if (rel != (unsigned)(cp.row[g] - first) * kSlotBytes + (unsigned)off) ++bad;
-                    if (cp.row[g] - first < 0 || cp.row[g] - first >= L::ROWS_PER_OP) ++bad;
+                    if (cp.row(g) < 0 || cp.row(g) >= L::BN || off < 0 || off + 16 > L::RB) ++bad;
+                    if (rel != (unsigned)(cp.row(g) - first) * kSlotBytes + (unsigned)off) ++bad;
+                    if (cp.row(g) - first < 0 || cp.row(g) - first >= L::ROWS_PER_OP) ++bad;
                     const int slot = byte / 16;
                     ++writes[slot];
-                    src_row[slot] = cp.row[g];
+                    src_row[slot] = cp.row(g);
                     src_chunk[slot] = off / 16;
                 }
             }
@@ -73,7 +73,8 @@ int check_layout() {
             std::vector<int> bank(8 * 64, 0);
             for (int lane = 0; lane < 64; ++lane) {
                 const Frag f = swizzled_frag<D>(lane);
-                const int off = f.k + kt * 32 * D + 8 * ((2 * kc) ^ f.kx);
+                // the kernel's expression (lane base per kc & 7, the rest immediate)
+                const int off = f.k + kt * 32 * D + 128 * (kc >> 3) + 8 * ((2 * (kc & 7)) ^ f.kx);
                 for (int j = 0; j < 8; ++j) {
                     int r, c;
                     held(0, off + j, &r, &c);
@@ -90,7 +91,8 @@ int check_layout() {
                 std::vector<int> bank(4 * 64, 0);
                 for (int lane = 0; lane < 64; ++lane) {
                     const Frag f = swizzled_frag<D>(lane);
-                    const int off = f.v + kc * 16 * D + 32 * (dt ^ f.vx) + 8 * hi * D;
+                    const int off =
+                        f.v + kc * 16 * D + 128 * (dt >> 2) + 32 * ((dt & 3) ^ f.vx) + 8 * hi * D;
                     const int g16 = lane >> 4;
                     const int row = 4 * (g16 >> 1) + ((lane & 15) >> 2) + 16 * kc + 8 * hi;
                     const int col = 32 * dt + 16 * (g16 & 1) + 4 * (lane & 3);

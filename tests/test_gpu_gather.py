@@ -70,7 +70,8 @@ def _check(w, path, waves=4, fp8_to=P.TO_16BIT, limit=None, what=""):
         assert bad.size == 0, f"{what} {name}: {len(bad)} mismatching elements, first {bad[:3]}"
 
 
-RING_CASES = [(64, 8), (64, 16), (128, 4), (128, 16), (128, 32), (64, 64)]
+RING_CASES = [(64, 8), (64, 16), (128, 4), (128, 16), (128, 32), (64, 64), (256, 2), (256, 16),
+              (256, 64)]
 
 
 @pytest.mark.parametrize("d,b", RING_CASES)

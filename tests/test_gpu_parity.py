@@ -471,7 +471,8 @@ def test_nan_poison_in_unused_blocks_and_tails_never_reaches_output():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["decode_batch", "chunked_prefill_mix", "long_prefill",
-                                  "variant_mix", "dense_prefill", "mha_prefill"])
+                                  "variant_mix", "dense_prefill", "mha_prefill",
+                                  "d256_prefill"])
 def test_named_workload_full_size(name):
     say(f"[gpu] {name}: generating")
     w = W.NAMED[name]()

@@ -103,6 +103,10 @@ constexpr int min_waves_per_simd(int d, int waves) {
 #ifndef UA_LDS_RING
 #define UA_LDS_RING 1
 #endif
+// largest head dim built with the ring
+#ifndef UA_LDS_RING_MAX_D
+#define UA_LDS_RING_MAX_D 256
+#endif
 // kv heads a stream-K worker workgroup serves together (a power of two; the
 // launch takes the largest that divides H_k)
 #ifndef UA_SK_HEADS
@@ -346,7 +350,10 @@ struct LdsGeom {
     static constexpr int OPS = 2 * BN * RB / 1024;  // copies per tile (K image, then V)
     static constexpr int GROUPS = OPS / 8;          // row groups per wave (a K and a V copy each)
     static constexpr int OPS_W = 2 * GROUPS;        // copies per wave per tile
-    static constexpr int STAGES = 3;
+    // three stages (two tiles in flight) where three fit beside two other
+    // workgroups' rings; at d = 256 a stage is 32 KB and two keep two
+    // workgroups resident per CU
+    static constexpr int STAGES = D > 128 ? 2 : 3;
     static constexpr int TILE_ELEMS = BN * D;       // one K or V image (16-bit elements)
     static constexpr uint32_t STAGE_BYTES = 4 * TILE_ELEMS;
     static_assert(OPS % 8 == 0, "four waves copy whole row groups");
@@ -387,23 +394,34 @@ __host__ __device__ inline Frag swizzled_frag(int lane) {
 template <int D>
 struct LdsCopy {
     typedef LdsGeom<D> L;
-    int row[L::GROUPS];
-    int koff[L::GROUPS], voff[L::GROUPS];  // byte offsets of the fetched chunks
+    // Groups g and g + KD have the same chunk permutation (their rows differ
+    // by a multiple of the permutations' periods), so a lane keeps KD K
+    // offsets and one V offset.
+    static constexpr int KD = D > 128 ? 2 : 1;
+    int wave, lane;
     // byte offsets from the group's first key row (that row's slot in the
     // caches is the copy's scalar base when every key of the tile is valid)
-    uint32_t krel[L::GROUPS], vrel[L::GROUPS];
+    uint32_t krel_[KD], vrel_;
 
-    __host__ __device__ void init(int wave, int lane, uint32_t slot_bytes) {
-        const int cs = lane % L::CPR;
-        for (int g = 0; g < L::GROUPS; ++g) {
-            row[g] = (wave + 4 * g) * L::ROWS_PER_OP + lane / L::CPR;
-            koff[g] = 16 * (cs ^ swz_k<D>(row[g]));
-            voff[g] = 16 * (cs ^ swz_v<D>(row[g]));
-            krel[g] = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)koff[g];
-            vrel[g] = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)voff[g];
-        }
+    // key row of group g and the byte offsets of its fetched K / V chunks
+    __host__ __device__ int row(int g) const { return (wave + 4 * g) * L::ROWS_PER_OP + lane / L::CPR; }
+    __host__ __device__ int koff(int g) const { return 16 * ((lane % L::CPR) ^ swz_k<D>(row(g))); }
+    __host__ __device__ int voff(int g) const { return 16 * ((lane % L::CPR) ^ swz_v<D>(row(g))); }
+    __host__ __device__ uint32_t krel(int g) const { return krel_[g % KD]; }
+    __host__ __device__ uint32_t vrel(int) const { return vrel_; }
+
+    __host__ __device__ void init(int wave_, int lane_, uint32_t slot_bytes) {
+        wave = wave_;
+        lane = lane_;
+        for (int g = 0; g < KD; ++g)
+            krel_[g] = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)koff(g);
+        vrel_ = (uint32_t)(lane / L::CPR) * slot_bytes + (uint32_t)voff(0);
     }
 };
+static_assert(swz_k<256>(0) == swz_k<256>(4 * 2 * LdsGeom<256>::ROWS_PER_OP) &&
+                  swz_k<128>(0) == swz_k<128>(4 * LdsGeom<128>::ROWS_PER_OP) &&
+                  swz_k<64>(0) == swz_k<64>(4 * LdsGeom<64>::ROWS_PER_OP),
+              "the K permutation repeats every KD groups");
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -469,19 +487,19 @@ __device__ __forceinline__ void lds_tile_issue(const LdsCopy<D>& cp, const unsig
             const uint64_t slot = ((uint64_t)(uint32_t)id[g] << lb) + (uint32_t)(first & bmask);
             const uint64_t off = slot * slot_bytes;
             const uint32_t m0 = m0_stage + (uint32_t)(wave + 4 * g) * 1024u;
-            lds_copy16_s(cp.krel[g], base_k + off, m0);
-            lds_copy16_s(cp.vrel[g], base_v + off, m0 + (uint32_t)(2 * L::TILE_ELEMS));
+            lds_copy16_s(cp.krel(g), base_k + off, m0);
+            lds_copy16_s(cp.vrel(g), base_v + off, m0 + (uint32_t)(2 * L::TILE_ELEMS));
         }
         return;
     }
 #pragma unroll
     for (int g = 0; g < L::GROUPS; ++g) {
-        const int key = min(t * L::BN + cp.row[g], s_k - 1);
+        const int key = min(t * L::BN + cp.row(g), s_k - 1);
         const uint64_t slot = ((uint64_t)(uint32_t)id[g] << lb) + (uint32_t)(key & bmask);
         const uint64_t off = slot * slot_bytes;
         const uint32_t m0 = m0_stage + (uint32_t)(wave + 4 * g) * 1024u;
-        lds_copy16(base_k + off + cp.koff[g], m0);
-        lds_copy16(base_v + off + cp.voff[g], m0 + (uint32_t)(2 * L::TILE_ELEMS));
+        lds_copy16(base_k + off + cp.koff(g), m0);
+        lds_copy16(base_v + off + cp.voff(g), m0 + (uint32_t)(2 * L::TILE_ELEMS));
     }
 }
 
@@ -599,14 +617,16 @@ __device__ __forceinline__ void qk_tile(const unsigned short* __restrict__ k_lds
         v8 a[D / 16];
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
-            const int off = SWZ ? fr.k + kt * 32 * D + 8 * ((2 * kc) ^ fr.kx)
+            // kx < 16, so chunks 16 and up keep their high bit: eight lane
+            // bases serve every kc, the rest is an immediate offset
+            const int off = SWZ ? fr.k + kt * 32 * D + 128 * (kc >> 3) + 8 * ((2 * (kc & 7)) ^ fr.kx)
                                 : fr.k + kt * 32 * KSTR + 16 * kc;
             a[kc] = *reinterpret_cast<const v8*>(&k_lds[off]);
         }
         sacc[kt] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) sacc[kt] = Q::mma(a[kc], qf[kc], sacc[kt]);
-        if constexpr (SWZ) {
+        if constexpr (SWZ && D <= 128) {
             // On the ring, keep four fragment reads ahead of the MFMA chain
             // (then one read per MFMA): the default schedule kept two, and
             // each MFMA waited on its read (measured about +0.6-3% on prefill).
@@ -709,7 +729,8 @@ __device__ __forceinline__ void pv_tile(const unsigned short* __restrict__ v_lds
     for (int kc = 0; kc < BN / 16; ++kc) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-            const int off = SWZ ? fr.v + kc * 16 * D + 32 * (dt ^ fr.vx)
+            // vx < 4: four lane bases, the rest immediate (as for K)
+            const int off = SWZ ? fr.v + kc * 16 * D + 128 * (dt >> 2) + 32 * ((dt & 3) ^ fr.vx)
                                 : fr.v + kc * 16 * VSTR + dt * 32;
             constexpr int HI = 8 * (SWZ ? D : VSTR);
             i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&v_lds[off]);
@@ -1035,10 +1056,11 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     // size so every stage address is a constant of the instructions.
     auto step = [&](auto stage_c, int t) {
         constexpr int ST = decltype(stage_c)::value;
-        // tile t has landed (tile t + 1 may still be in flight) and every
-        // wave is done with tile t - 1, whose stage is refilled next
+        // tile t has landed (with three stages tile t + 1 may still be in
+        // flight) and every wave is done with tile t - 1, whose stage is
+        // refilled next
         if (t + 1 < t_hi)
-            lds_tile_barrier<L::OPS_W>();
+            lds_tile_barrier<(S - 2) * L::OPS_W>();
         else
             lds_tile_barrier<0>();
         const int t_next = t + S - 1;
@@ -1055,11 +1077,18 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
                                                 l_run, key0, need_mask, ri.rc, fr, half);
         }
     };
-    static_assert(S == 3, "the loop is unrolled for three stages");
-    for (int t = t_lo; t < t_hi; t += 3) {
-        step(std::integral_constant<int, 0>{}, t);
-        if (t + 1 < t_hi) step(std::integral_constant<int, 1>{}, t + 1);
-        if (t + 2 < t_hi) step(std::integral_constant<int, 2>{}, t + 2);
+    if constexpr (S == 3) {
+        for (int t = t_lo; t < t_hi; t += 3) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < t_hi) step(std::integral_constant<int, 1>{}, t + 1);
+            if (t + 2 < t_hi) step(std::integral_constant<int, 2>{}, t + 2);
+        }
+    } else {
+        static_assert(S == 2, "the loop is unrolled for two or three stages");
+        for (int t = t_lo; t < t_hi; t += 2) {
+            step(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < t_hi) step(std::integral_constant<int, 1>{}, t + 1);
+        }
     }
 
     if (!wave_active) return;
@@ -1930,9 +1959,13 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         }
     } else {
         // 16-bit K/V in four-wave workgroups take the LDS ring when one
-        // wave-wide copy's key rows always share a block (d <= 128: at
-        // d = 256 the O and Q registers leave no room for the ring's)
-        constexpr bool ring_built = UA_LDS_RING && NW == 4 && BN == LdsGeom<D>::BN && !FP8 && D <= 128;
+        // wave-wide copy's key rows always share a block.  At d = 256 only
+        // without score transforms: the swizzled tiles' lane addresses cost
+        // registers the padded ones do not, and with softcap or ALiBi the
+        // ring's variant spills (measured 1-4% slower than the register path
+        // on softcap prefill, against 7-11% faster without transforms).
+        constexpr bool ring_built = UA_LDS_RING && NW == 4 && BN == LdsGeom<D>::BN && !FP8 &&
+                                    D <= UA_LDS_RING_MAX_D && (D <= 128 || XF == kXfNone);
         const bool ring = ring_built && (1 << p.block_size_log2) >= LdsGeom<D>::ROWS_PER_OP &&
                           p.kv_slot_stride * 2 * LdsGeom<D>::ROWS_PER_OP < (int64_t(1) << 31);
         const bool split = l.path == 3;

@@ -399,6 +399,14 @@ def _spec_mha_prefill(seed):
                         causal=False, dense=True))
 
 
+def _spec_d256_prefill(seed):
+    """Causal prefill at head dim 256: 1 sequence S_q = S_k = 8192 plus 4 of
+    2048, H_q=16, H_k=8 (g=2), d=256, b=64, bf16, no other flags."""
+    lens = [8192, 2048, 2048, 2048, 2048]
+    return dict(q_lens=lens, seq_lens=lens, rng=None,
+                kw=dict(num_q_heads=16, num_kv_heads=8, head_dim=256, block_size=64))
+
+
 NAMED_SPECS = {
     "tiny_varlen": (1, _spec_tiny_varlen),
     "decode_batch": (2, _spec_decode_batch),
@@ -407,6 +415,7 @@ NAMED_SPECS = {
     "variant_mix": (5, _spec_variant_mix),
     "dense_prefill": (6, _spec_dense_prefill),
     "mha_prefill": (7, _spec_mha_prefill),
+    "d256_prefill": (8, _spec_d256_prefill),
 }
 
 
@@ -451,6 +460,7 @@ NAMED = {
     "variant_mix": variant_mix,
     "dense_prefill": lambda seed=6: named("dense_prefill", seed),
     "mha_prefill": lambda seed=7: named("mha_prefill", seed),
+    "d256_prefill": lambda seed=8: named("d256_prefill", seed),
 }
 
 
