@@ -237,6 +237,41 @@ def test_shape_rule(name, path, split):
     assert ws < (3 << 30)
 
 
+RING_POLICY = [
+    # (H_q, H_k, d, b, extra flags, decode rows, class split expected)
+    (32, 8, 128, 16, 0, 40, 0),                  # d <= 128 ring: one launch
+    (32, 8, 128, 2, 0, 40, 1),                   # blocks below one copy's 4 rows
+    (16, 8, 256, 32, 0, 96, 0),                  # d = 256 ring, grid fills a round
+    (16, 2, 256, 32, 0, 64, 1),                  # d = 256 ring, grid too small
+    (16, 8, 256, 32, B.UA_FLAG_SOFTCAP, 96, 1),  # d = 256 with a transform
+    (16, 8, 256, 32, B.UA_FLAG_ALIBI, 96, 1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(RING_POLICY)))
+def test_mixed_batch_policy(i):
+    """Decode rows plus four 512-query chunks: LDS-ring batches (16-bit K/V,
+    blocks of at least 512 / d keys, at d = 256 only without softcap, ALiBi
+    or QQ-bias) stay one 2D launch when their full grid fills a resident
+    round; other wide batches, and d = 256 ring batches that do not fill it,
+    send the decode rows to the concurrent stream-K launch.  A d <= 128 ring
+    batch never splits."""
+    hq, hk, d, b, extra, n_dec, want = RING_POLICY[i]
+    sk_max = 8192
+    desc = _desc(num_q_heads=hq, num_kv_heads=hk, head_dim=d, block_size=b,
+                 flags=B.UA_FLAG_CAUSAL | extra, softcap=30.0 if extra & B.UA_FLAG_SOFTCAP else 0.0,
+                 num_blocks=(n_dec + 4) * sk_max // b, max_num_seqs=n_dec + 4,
+                 max_blocks_per_seq=sk_max // b, max_total_q=n_dec + 4 * 512, max_seqlen_k=sk_max)
+    h = B.ua_create_problem(desc)
+    try:
+        plan = B.ua_query_plan(h, n_dec + 4, n_dec + 4 * 512, 512, sk_max)
+    finally:
+        B.ua_destroy_problem(h)
+    assert plan.path == 2 and plan.class_split == want
+    if want:
+        assert plan.stream_k == 1
+
+
 def test_segment_override_selects_the_segmented_split():
     plan, _ = _named_plan("decode_batch", split_segment_tiles=16)
     assert plan.path == 3 and plan.stream_k == 0 and plan.tiles_per_segment == 16

@@ -180,6 +180,9 @@ MIXED = [
     ("fp8_d128_softcap", dict(kv_dtype=W.DT_FP8_E4M3, softcap=20.0), (32, 8, 128, 16), 1),
     ("bf16_d256_window", dict(window=150, use_sinks=True), (16, 4, 256, 32), 1),
     ("fp8_d64_g4", dict(kv_dtype=W.DT_FP8_E4M3), (16, 4, 64, 16), 1),
+    # blocks of 2 keys are below one ring copy's 4 rows: register path, split
+    ("bf16_d128_b2", dict(use_sinks=True), (16, 4, 128, 2), 1),
+    ("bf16_d256_softcap", dict(softcap=25.0), (16, 8, 256, 16), 1),
 ]
 
 
@@ -202,6 +205,24 @@ def test_mixed_decode_and_chunks(i):
                 num_kv_heads=hk, head_dim=d, block_size=b, rng=rng, **flags)
     _, plan = _full_check(w, "auto")
     assert plan.class_split == want_split
+
+
+def test_d256_ring_batch_in_one_launch():
+    """A d = 256 16-bit batch without score transforms whose full grid fills a
+    resident round stays one 2D launch on the two-stage LDS ring, decode
+    q-blocks and chunks together."""
+    rng = np.random.default_rng(420)
+    n_dec = 96
+    dec_k = rng.integers(1, 500, size=n_dec, endpoint=True)
+    ch_q = rng.integers(40, 120, size=4, endpoint=True)
+    ctx = rng.integers(0, 300, size=4, endpoint=True)
+    q_lens = np.concatenate([np.ones(n_dec, np.int64), ch_q])
+    order = rng.permutation(q_lens.size)
+    w = W.build("d256_ring_mixed", 420, q_lens[order], np.concatenate([dec_k, ctx + ch_q])[order],
+                num_q_heads=16, num_kv_heads=8, head_dim=256, block_size=16, rng=rng,
+                use_sinks=True, window=400)
+    _, plan = _full_check(w, "auto")
+    assert plan.path == 2 and plan.class_split == 0
 
 
 @pytest.mark.parametrize("d,b", [(64, 1), (64, 4), (128, 2), (128, 4), (64, 8)])

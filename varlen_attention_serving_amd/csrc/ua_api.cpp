@@ -192,21 +192,31 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         const int64_t wide_grid = (int64_t)d.num_kv_heads * (total_q / w.block_q + 1);
         two_d = wide_grid >= kWideResidentPerCU * kNumCUs;
     }
-    // Wide q-blocks of 16-bit K/V with d <= 128 run on the LDS ring, which
-    // streams a decode-shaped q-block's keys at HBM speed inside the same
-    // launch: keep the whole batch in one 2D launch once its full grid
-    // (every sequence's slots) fills a resident round.
-    const bool ring = !P.fp8 && d.head_dim <= 128;
-    if (!small && ring && (int64_t)d.num_kv_heads * w.slots >= kWideResidentPerCU * kNumCUs)
-        two_d = true;
+    // Wide q-blocks of 16-bit K/V run on the LDS ring (at d = 256 only
+    // without score transforms; blocks must hold one copy's 512 / d key
+    // rows), which streams a decode-shaped q-block's keys at HBM speed inside
+    // the same launch: keep the whole batch in one 2D launch once its full
+    // grid (every sequence's slots) fills a resident round.
+    const uint32_t score_xf = UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_QQ_BIAS;
+    const bool ring = !P.fp8 && (d.head_dim <= 128 || !(d.flags & score_xf)) &&
+                      (int64_t(1) << P.log2_block) * d.head_dim >= 512 &&
+                      (int64_t)d.num_kv_heads * d.head_dim * 2 * (512 / d.head_dim) < (int64_t(1) << 31);
+    const bool ring_fills =
+        !small && ring && (int64_t)d.num_kv_heads * w.slots >= kWideResidentPerCU * kNumCUs;
+    if (ring_fills) two_d = true;
     if (force2) two_d = true;
     if (force3) two_d = false;
 
-    // Otherwise (register-staged wide launches: fp8 K/V or d = 256) the
-    // decode-shaped sequences of a wide batch go to the stream-K kernel,
-    // beside the wide launch that keeps the rest.
-    const bool split = !small && !ring && !force2 && !force3 && pl.small_block_q > 0 && sk_fits &&
-                       d.split_segment_tiles == 0;
+    // Otherwise the decode-shaped sequences of a wide batch go to the
+    // stream-K kernel, beside the wide launch that keeps the rest: for
+    // register-staged wide launches (fp8 K/V, d = 256 with score transforms,
+    // blocks below one copy's rows) and for d = 256 ring batches too small
+    // to fill a round (measured with 64 decode rows and 4 chunks of 512:
+    // H_k = 8 fills it, one launch 0.70 ms against 0.75 split; H_k = 2 does
+    // not, split 0.353 ms against 0.385 in one launch).  A d <= 128 ring batch
+    // keeps one launch (the split measured slower there).
+    const bool split = !small && !ring_fills && (!ring || d.head_dim > 128) && !force2 &&
+                       !force3 && pl.small_block_q > 0 && sk_fits && d.split_segment_tiles == 0;
     w.class_mode = split ? 2 : 0;
     // Beside a concurrent stream-K launch the wide q-blocks need no segments
     // to fill the device (measured: variant_mix 0.148 -> 0.125 ms unsplit).
