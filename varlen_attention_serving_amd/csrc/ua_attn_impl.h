@@ -1364,10 +1364,18 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
     };
     begin_pair(pc);
 
+    // Each wave owns its tiles and its LDS operations run in order, so the
+    // waves need no barrier for correctness.  With 16-bit K/V they still meet
+    // once per tile: in step, the worker's waves (its kv heads) read each key
+    // row's heads together, contiguous in the cache (measured: decode_batch
+    // 0.216 -> 0.223 ms without the barriers).  With fp8 K/V, where each wave
+    // also converts its tile, they run free (fp8 decode at d = 128: 0.145 ->
+    // 0.129 ms).
+    constexpr bool WG_SYNC = !FP8;
     for (int64_t x = A; x < B; ++x) {
-        __syncthreads();
+        if (WG_SYNC) __syncthreads(); else asm volatile("" ::: "memory");
         ld.store(k_lds, v_lds);
-        __syncthreads();
+        if (WG_SYNC) __syncthreads(); else asm volatile("" ::: "memory");
         if (x + 1 < B) {
             ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb);
