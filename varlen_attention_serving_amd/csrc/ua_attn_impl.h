@@ -1368,14 +1368,14 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
     // waves need no barrier for correctness.  With 16-bit K/V they still meet
     // once per tile: in step, the worker's waves (its kv heads) read each key
     // row's heads together, contiguous in the cache (measured: decode_batch
-    // 0.216 -> 0.223 ms without the barriers).  With fp8 K/V, where each wave
-    // also converts its tile, they run free (fp8 decode at d = 128: 0.145 ->
+    // 0.216 -> 0.223 ms without a barrier).  With fp8 K/V, where each wave
+    // also converts its tile, they run free (fp8 decode at d = 128: 0.144 ->
     // 0.129 ms).
     constexpr bool WG_SYNC = !FP8;
     for (int64_t x = A; x < B; ++x) {
         if (WG_SYNC) __syncthreads(); else asm volatile("" ::: "memory");
         ld.store(k_lds, v_lds);
-        if (WG_SYNC) __syncthreads(); else asm volatile("" ::: "memory");
+        asm volatile("" ::: "memory");
         if (x + 1 < B) {
             ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb);
@@ -1629,7 +1629,7 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
     static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
 
     // one V tile per wave (dynamic LDS sized at launch); the waves of a worker
-    // share nothing else, so they need no barrier
+    // share nothing else
     extern __shared__ __attribute__((aligned(16))) unsigned short sk16_lds[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     unsigned short* v_lds = sk16_lds + wave * (BN * G::VSTR);
@@ -1696,9 +1696,16 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
     };
     begin_pair(pc);
 
+    // The worker's waves meet once per tile with 16-bit K/V, as in the 32-row
+    // engine (measured: bf16 decode at d = 256, 0.229 -> 0.217 ms with four kv
+    // heads per worker, 0.419 -> 0.404 with eight); each wave's own LDS order
+    // needs no barrier, and fp8 workers run free (a barrier there cost 1%,
+    // and 4% on variant_mix).
+    constexpr bool WG_SYNC = !FP8;
     for (int64_t x = A; x < B; ++x) {
         // this tile's V into LDS (the previous tile's reads are done: one
         // wave, LDS operations in order), then the next tile's loads
+        if (WG_SYNC) __syncthreads();
         ld.store_v(v_lds);
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
