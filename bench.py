@@ -102,8 +102,8 @@ ATTENTION_KERNELS = ("ua_decode_sk_kernel", "ua_decode16_kernel", "ua_attn_lds_k
                      "ua_attn_kernel")
 
 
-def _plan_path(args):
-    """Path of the bench's plan for the workload (host-side query, no GPU)."""
+def _plan(args):
+    """The bench's plan for the workload (host-side query, no GPU)."""
     from varlen_attention_serving_amd import binding as B
     from varlen_attention_serving_amd import device as D
     from varlen_attention_serving_amd import workloads as W
@@ -111,7 +111,7 @@ def _plan_path(args):
     extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[args.force]
     h = B.ua_create_problem(D.problem_desc(w, extra, split_segment_tiles=args.segment_tiles))
     try:
-        return B.ua_query_plan(h, w.num_seqs, w.total_q, w.max_seqlen_q, w.max_seqlen_k).path
+        return B.ua_query_plan(h, w.num_seqs, w.total_q, w.max_seqlen_q, w.max_seqlen_k)
     finally:
         B.ua_destroy_problem(h)
 
@@ -142,10 +142,18 @@ def summarize_traffic(args):
     # split's other launch may find no rows of its class)
     att = max((k for k in out["kernels"] if k in ATTENTION_KERNELS),
               key=lambda k: out["kernels"][k]["bytes_read"])
-    out["attention_kernel"] = att
-    out["path"] = _plan_path(args)
-    a = out["kernels"][att]
-    out["bytes_per_launch"] = a["bytes_read"] + a["bytes_written"]
+    plan = _plan(args)
+    out["path"] = plan.path
+    if plan.class_split:
+        # the timed span of a class split holds both attention launches and
+        # the stream-K reduce: price their traffic together
+        out["attention_kernel"] = "+".join(sorted(out["kernels"]))
+        out["bytes_per_launch"] = sum(k["bytes_read"] + k["bytes_written"]
+                                      for k in out["kernels"].values())
+    else:
+        out["attention_kernel"] = att
+        a = out["kernels"][att]
+        out["bytes_per_launch"] = a["bytes_read"] + a["bytes_written"]
     path = os.path.join(ROOT, "profiles", f"{args.workload}_hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
