@@ -68,6 +68,93 @@ def algorithmic_work(w):
                 pairs=pairs, visited_keys=int(visited.sum()))
 
 
+class ClockSampler:
+    """GFX (SCLK) and memory (MCLK) clocks of the benchmarked GPU, sampled by
+    amdsmi on a host thread while the timed steps run (the pages note a
+    25-30% automatic clock swing, so a figure without its clock is hard to
+    compare).  Any failure leaves a reason instead of samples."""
+
+    def __init__(self, period_s=0.001):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self.handle = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            import torch
+            self.smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            want = (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", -1),
+                    getattr(props, "pci_device_id", -1))
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            if self.handle is None:
+                self.error = f"no amdsmi device matches PCI {want}"
+        except Exception as e:  # no amdsmi, no permission, ...
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        # the firmware's metrics table: one current gfx clock per XCD, and the
+        # memory (UMC) clock
+        mt = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        xcd = [float(v) for v in (mt.get("current_gfxclks") or [])
+               if isinstance(v, (int, float)) and v > 0]
+        g = float(np.mean(xcd)) if xcd else float(mt["current_gfxclk"])
+        return g, float(mt["current_uclk"])
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read() + (time.perf_counter(),))
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self.handle is not None:
+            try:
+                self.smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        if not self.samples:
+            return {"samples": 0, "error": self.error or "no samples"}
+        s = np.array(self.samples)
+        window = float(s[-1, 2] - s[0, 2])
+        # The metrics table refreshes slowly: values read before its first
+        # change after the start describe the idle GPU, so they are dropped.
+        moved = np.nonzero(s[:, 0] != s[0, 0])[0]
+        if len(moved) == 0:
+            return {"samples": len(s), "window_s": round(window, 3),
+                    "note": "the firmware clock table did not refresh during the timed steps "
+                            "(it lags by tens of ms); run more --steps to read clocks"}
+        live = s[moved[0]:]
+        return {"samples": len(live), "window_s": round(window, 3),
+                "gfx_mhz_median": round(float(np.median(live[:, 0])), 1),
+                "gfx_mhz_min": round(float(live[:, 0].min()), 1),
+                "gfx_mhz_max": round(float(live[:, 0].max()), 1),
+                "mem_mhz_median": round(float(np.median(live[:, 1])), 1)}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
@@ -218,6 +305,9 @@ def main():
                     help="record the kernel-timing events on every N-th timed step (warm runs)")
     ap.add_argument("--segment-tiles", type=int, default=0,
                     help="split-KV segment length in KV tiles (0 = the plan's choice)")
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="seconds of untimed replay after timing during which amdsmi "
+                         "samples the GPU clocks (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -329,6 +419,23 @@ def main():
         r_unit = "TFLOP/s"
     traffic = load_traffic(args.workload, plan.path)
 
+    # Clocks under this load: the firmware's table refreshes too slowly to be
+    # read inside a short timed region, so sample it over an untimed replay of
+    # the same step after the timing.
+    clock_info = None
+    if args.clock_seconds > 0:
+        clocks = ClockSampler()
+        if clocks.handle is not None:
+            reps = int(min(50000, max(1, args.clock_seconds * 1e3 / max(ms_per_step, 1e-3))))
+            clocks.start()
+            for i in range(reps):
+                B.ua_run(handle, run_args, stream.cuda_stream)
+                if flush is not None:
+                    flush.fill_(i & 0xFF)
+            torch.cuda.synchronize()
+        clock_info = clocks.stop()
+        clock_info["replay"] = f"untimed replay of the step for about {args.clock_seconds:g} s"
+
     cpu = None
     if args.cpu_seconds > 0:
         print(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
@@ -371,6 +478,7 @@ def main():
             "attention_kernel_ms_min": round(float(np.min(attn_each)), 5),
             "cache": "cold (512 MiB flush between steps)" if args.cold else "warm",
             "roofline_frac_whole_step": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
+            "clocks": clock_info,
         },
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
                      "unit": r_unit, "frac": round(achieved / peak, 4), "traffic": traffic},
