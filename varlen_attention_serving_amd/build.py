@@ -66,7 +66,46 @@ def build(jobs: int = 0, verbose: bool = True, defines=(), out: str = LIB,
     return out
 
 
+def resources(build_dir: str = BUILD_DIR) -> dict:
+    """Per-kernel resources as the compiler reports them for gfx950 (VGPRs,
+    AGPRs, SGPRs, spills, scratch, static LDS and its occupancy estimate,
+    which ignores dynamic LDS), from a device-only compile of every kernel
+    translation unit with the kernel-resource-usage remarks."""
+    os.makedirs(build_dir, exist_ok=True)
+    keys = {"TotalSGPRs": "sgpr", "VGPRs": "vgpr", "AGPRs": "agpr",
+            "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy",
+            "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+            "LDS Size [bytes/block]": "lds_static"}
+    out = {}
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".res.o")
+        cmd = [HIPCC, *COMMON, "--offload-device-only", "-Rpass-analysis=kernel-resource-usage",
+               "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        cur = None
+        for line in r.stderr.splitlines():
+            if "remark:" not in line or "kernel-resource-usage" not in line:
+                continue
+            body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+            name, _, val = body.partition(":")
+            name, val = name.strip(), val.strip()
+            if name == "Function Name":
+                cur = out.setdefault(val, {})
+            elif cur is not None and name in keys:
+                cur[keys[name]] = int(val) if val.isdigit() else val
+    return out
+
+
 if __name__ == "__main__":
-    build()
-    if shutil.which("nm"):
-        pass
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        pats = sys.argv[2:]
+        for name, r in sorted(resources().items()):
+            if pats and not any(s in name for s in pats):
+                continue
+            print(f"{name}  " + "  ".join(f"{k}={v}" for k, v in r.items()))
+    else:
+        build()
