@@ -38,3 +38,54 @@ def test_clock_summary_without_samples_gives_the_reason():
     c.error = "AmdSmiLibraryException: driver not loaded"
     s = c.stop()
     assert s["samples"] == 0 and "driver" in s["error"]
+
+
+def _write_counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, counter, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def _summarize(tmp_path, monkeypatch, class_split):
+    import argparse
+    import json
+    import types
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_plan",
+                        lambda args: types.SimpleNamespace(path=2, class_split=class_split))
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    cfetch, cwrite = tmp_path / "cf.csv", tmp_path / "cw.csv"
+    # the copy of 1 MiB reads 512 KiB and writes 1024 KiB as counted: scales 2 and 1
+    _write_counter_csv(cfetch, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
+    _write_counter_csv(cwrite, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    _write_counter_csv(fetch, [("ua_attn_kernel<...>", "FETCH_SIZE", 10.0),
+                               ("ua_decode16_kernel<...>", "FETCH_SIZE", 100.0),
+                               ("ua_decode16_kernel<...>", "FETCH_SIZE", 102.0),
+                               ("ua_reduce_kernel<...>", "FETCH_SIZE", 5.0)])
+    _write_counter_csv(write, [("ua_attn_kernel<...>", "WRITE_SIZE", 8.0),
+                               ("ua_decode16_kernel<...>", "WRITE_SIZE", 3.0),
+                               ("ua_reduce_kernel<...>", "WRITE_SIZE", 1.0)])
+    args = argparse.Namespace(workload="variant_mix", summarize_traffic=[
+        str(fetch), str(write), str(cfetch), str(cwrite), str(1 << 20)])
+    bench.summarize_traffic(args)
+    return json.load(open(tmp_path / "profiles" / "variant_mix_hbm_traffic.json"))
+
+
+def test_traffic_of_one_launch_is_its_dominant_attention_kernel(tmp_path, monkeypatch):
+    t = _summarize(tmp_path, monkeypatch, class_split=0)
+    assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
+    assert t["attention_kernel"] == "ua_decode16_kernel"
+    # decode16: (100 + 102) / 2 KiB read x 2, 3 KiB written
+    assert t["bytes_per_launch"] == 101 * 1024 * 2 + 3 * 1024
+
+
+def test_traffic_of_a_class_split_sums_its_timed_span(tmp_path, monkeypatch):
+    t = _summarize(tmp_path, monkeypatch, class_split=1)
+    assert t["attention_kernel"] == "ua_attn_kernel+ua_decode16_kernel+ua_reduce_kernel"
+    read = (10 + 101 + 5) * 1024 * 2
+    written = (8 + 3 + 1) * 1024
+    assert t["bytes_per_launch"] == read + written
