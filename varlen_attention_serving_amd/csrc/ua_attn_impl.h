@@ -177,6 +177,25 @@ __device__ __forceinline__ float xor32(float x) {
     return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// max(x of lane l, x of lane l ^ 32) in every lane.  One swap of x with itself
+// leaves x's low half in both halves of one result and its high half in both
+// halves of the other; the max is taken in assembly so no canonicalisation of
+// the swapped values is added (scores are finite or -inf, never NaN).
+__device__ __forceinline__ float max_halves(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(r[0]), "v"(r[1]));
+    return m;
+}
+
+// The running max a row starts from when no sink logit sets it: a finite
+// stand-in for -inf, so exponents 2^(x c - m) need no guard.  Every finite
+// score exceeds it by more than the lazy-rescale slack, so the first tile with
+// a visible key moves the max (and re-bases O and l, both still 0); a row that
+// never sees a key keeps l = 0 and gets O = 0 and LSE = -inf.
+constexpr float kMaxStart = -1.0e30f;
+
 // Number of indices j in [1, n) with pred(j); every lane of the wave gets it.
 template <typename Pred>
 __device__ __forceinline__ int wave_count(int n, Pred pred) {
@@ -680,7 +699,7 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
     }
-    mt = fmaxf(mt, xor32(mt)) * c;
+    mt = max_halves(mt) * c;
     // Lazy reference max: exponents are taken against m_run, which moves only
     // when some row's tile max exceeds it by more than kLazyRescale (log2
     // units).  Softmax is shift-invariant, so o and l stay exact relative to
@@ -704,13 +723,12 @@ __device__ __forceinline__ void softmax_exp(const UaKernelParams& p, const f32x1
                                             typename QType<QT>::v8 (&pf)[BN / 16]) {
     typedef QType<QT> Q;
     const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
         const int kt = kc >> 1, q8 = (kc & 1) * 8;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            pf[kc][j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_use));
+            pf[kc][j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_run));
         // the denominator sums the same rounded p the PV product uses
 #pragma unroll
         for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[kc][j], pf[kc][j + 1], l_run);
@@ -930,7 +948,7 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
     load_q<D, QT>(p, ri, half, qf);
 
     // ---- running softmax state (log2 units) ----
-    float m_run = -INFINITY;
+    float m_run = kMaxStart;
     float l_run = 0.0f;
     if (!SPLIT && (p.flags & UA_FLAG_SINKS)) {
         // the sink is one more softmax column: start from (m, l) = (sink, 1)
@@ -1023,7 +1041,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     v8 qf[D / 16];
     load_q<D, QT>(p, ri, half, qf);
 
-    float m_run = -INFINITY;
+    float m_run = kMaxStart;
     float l_run = 0.0f;
     if (!SPLIT && (p.flags & UA_FLAG_SINKS)) {
         m_run = p.sinks[ri.head] * kLog2e;
@@ -1357,7 +1375,7 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         ri = row_info(p, lane & 31, head(q), q.q_start, q.q_len, q.s_k, 0);
         kr = key_range(p.flags, p.window, q.s_k, q.s_k - q.q_len, 0, q.q_len - 1);
         load_q<D, QT>(p, ri, half, qf);
-        m_run = -INFINITY;
+        m_run = kMaxStart;
         l_run = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) oacc[dt] = f32x16{};
@@ -1581,7 +1599,7 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
             mt = fmaxf(mt, sv);
         }
     mt = fmaxf(mt, xor16(mt));
-    mt = fmaxf(mt, xor32(mt)) * c;
+    mt = max_halves(mt) * c;
     // lazy reference max, as in the 32-row engine
     if (__ballot(mt > m_run + kLazyRescale)) {
         const float m_new = fmaxf(m_run, mt);
@@ -1592,11 +1610,10 @@ __device__ __forceinline__ void softmax_pv16(const UaKernelParams& p, f32x4 (&sa
         for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
         m_run = m_new;
     }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
     v8 pf;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        pf[j] = (QT)fast_exp2(__builtin_fmaf(sacc[j >> 2][j & 3], c, -m_use));
+        pf[j] = (QT)fast_exp2(__builtin_fmaf(sacc[j >> 2][j & 3], c, -m_run));
 #pragma unroll
     for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[j], pf[j + 1], l_run);
 #pragma unroll
@@ -1689,7 +1706,7 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
             if (ri.ok) w = *reinterpret_cast<const u32x4*>(qp + 32 * k2);
             qf[k2] = __builtin_bit_cast(v8, w);
         }
-        m_run = -INFINITY;
+        m_run = kMaxStart;
         l_run = 0.0f;
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) oacc[db] = f32x4{};
