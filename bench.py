@@ -287,6 +287,209 @@ def _subset(w, s):
     return sub
 
 
+def cpu_baseline_rows(w, budget_s, chunk=256):
+    """The oracle, untuned, on seeded random (token, head) rows of the batch,
+    chunk by chunk until about `budget_s` of wall time (for batches whose
+    sequences are too long to run whole); reported work is counted per row."""
+    import oracle
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(321)
+    vis = np.concatenate([_visible(w, s) for s in range(w.num_seqs)]) if w.num_seqs else []
+    row_bytes = 2 * w.head_dim * (1 if w.kv_dtype == 2 else 2)
+    done_flops = done_bytes = rows_done = 0
+    t_total = 0.0
+    while t_total < budget_s:
+        rows = rng.integers(0, w.total_q * w.num_q_heads, size=chunk)
+        t0 = time.perf_counter()
+        oracle.rows(w, rows, nthreads=threads)
+        t_total += time.perf_counter() - t0
+        keys = vis[rows // w.num_q_heads]
+        done_flops += int(keys.sum()) * 4 * w.head_dim
+        done_bytes += int(keys.sum()) * row_bytes + 4 * w.head_dim * len(rows)
+        rows_done += len(rows)
+    return dict(seconds=t_total, bytes=done_bytes, flops=done_flops, rows=rows_done,
+                cores=threads)
+
+
+def _visible(w, s):
+    """Keys visible to each local query row of sequence s."""
+    ql, sk = int(w.q_lens[s]), int(w.seq_lens[s])
+    q_abs = sk - ql + np.arange(ql, dtype=np.int64)
+    kmax = np.minimum(q_abs, sk - 1) if w.causal else np.full(ql, sk - 1)
+    kmin = np.maximum(q_abs - w.window + 1, 0) if w.window > 0 else np.zeros(ql, np.int64)
+    return np.maximum(kmax - kmin + 1, 0)
+
+
+class Runner:
+    """One workload on the device: its batch, problem handle and plan."""
+
+    def __init__(self, name, force="auto", segment_tiles=0):
+        from varlen_attention_serving_amd import binding as B
+        from varlen_attention_serving_amd import device as D
+        from varlen_attention_serving_amd import workloads as W
+        import torch
+        self.B, self.torch = B, torch
+        print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+        self.name = name
+        self.w = w = W.named(name)
+        extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[force]
+        self.batch = D.DeviceBatch(w)
+        self.ua = D.UnifiedAttention(D.problem_desc(w, extra, split_segment_tiles=segment_tiles))
+        self.plan = self.ua.plan(w)
+        self.work = algorithmic_work(w)
+        self.t_hbm = self.work["bytes"] / (HBM_PEAK_GBS * 1e9)
+        self.t_mfma = self.work["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+        self.bound = "hbm" if self.t_hbm >= self.t_mfma else "mfma"
+        self.stream = torch.cuda.current_stream()
+        self.args = self.batch.run_args(self.ua.workspace)
+
+    def step(self):
+        self.B.ua_run(self.ua.handle, self.args, self.stream.cuda_stream)
+
+    def time(self, steps, warmup, every=4, flush=None):
+        """Warm-up, then `steps` timed steps.  HIP events around the kernels
+        of every `every`-th step (every step with a flush); with `flush` (a
+        callable that evicts the caches) it runs before each step, outside
+        the events, and the step time is the events' sum."""
+        torch = self.torch
+        print(f"[bench] {self.name}: plan path={self.plan.path} split={self.plan.class_split} "
+              f"stream_k={self.plan.stream_k} waves={self.plan.waves} "
+              f"segments={self.plan.num_segments}; warmup {warmup}, "
+              f"{steps} steps{' (cold)' if flush else ''}", file=sys.stderr, flush=True)
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        # Recording events costs GPU time (about 10 us per step on the decode
+        # batch), so warm runs time the kernels on every `every`-th step only
+        # and leave the other steps as the workload runs in service.
+        every = 1 if flush else max(1, every)
+        sampled = list(range(0, steps, every))
+        evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+        for trio in evs.values():
+            for e in trio:
+                e.record(self.stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush()
+            for j in range(3):
+                self.args.timing_events[j] = evs[i][j].cuda_event if i in evs else None
+            self.step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for j in range(3):
+            self.args.timing_events[j] = None
+        attn = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])
+        whole = np.array([evs[i][0].elapsed_time(evs[i][2]) for i in sampled])
+        return dict(wall_ms=wall * 1e3 / steps, attn=attn, whole=whole, sampled=len(sampled))
+
+    def figures(self, t):
+        """Throughput and roofline from one timing: `value` over the wall
+        clock (warm) or the summed events (cold); the roofline prices the
+        attention kernel alone over its own events."""
+        work, plan = self.work, self.plan
+        attn_ms = float(np.mean(t["attn"]))
+        whole_ms = float(np.mean(t["whole"]))
+        if self.bound == "hbm":
+            per = lambda units, ms: units / (ms * 1e-3) / 1e9
+            units = work["bytes"]
+            # a split run's reduce writes O: the attention kernel does not
+            kernel_units = units - (work["o_bytes"] if plan.path == 3 else 0)
+            peak, unit = HBM_PEAK_GBS, "GB/s"
+        else:
+            per = lambda units, ms: units / (ms * 1e-3) / 1e12
+            units = kernel_units = work["flops"]
+            peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved = per(kernel_units, attn_ms)
+        return dict(attn_ms=attn_ms, whole_ms=whole_ms, unit=unit, peak=peak,
+                    achieved=achieved, frac=achieved / peak,
+                    value_wall=per(units, t["wall_ms"]), value_events=per(units, whole_ms),
+                    frac_whole_forward=max(self.t_hbm, self.t_mfma) / (whole_ms * 1e-3))
+
+    def roofline(self, f, traffic_workload=None):
+        name = traffic_workload or self.name
+        traffic = load_traffic(name, self.plan.path)
+        return {"bound": self.bound, "achieved": round(f["achieved"], 3), "peak": f["peak"],
+                "unit": f["unit"], "frac": round(f["frac"], 4), "traffic": traffic,
+                "scope": ("the attention kernel alone, over HIP events on its stream"
+                          + ("; the split-KV reduce (which writes O) and O's bytes excluded"
+                             if self.plan.path == 3 and self.bound == "hbm" else "")),
+                "traffic_source": (f"profiles/{name}_hbm_traffic.json: rocprofv3 --pmc "
+                                   "FETCH_SIZE + WRITE_SIZE per launch on these kernel sources"
+                                   if traffic is not None else
+                                   "no counter summary on the current kernel sources")}
+
+    def config(self):
+        w, plan, work = self.w, self.plan, self.work
+        return {"workload": self.name,
+                "num_seqs": w.num_seqs, "total_q": w.total_q, "max_seqlen_k": w.max_seqlen_k,
+                "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                "head_dim": w.head_dim, "block_size": w.block_size,
+                "kv_layout": "dense (cu_seqlens_k)" if w.dense else "paged (block table)",
+                "path": {2: "2d", 3: "3d-split-kv"}[plan.path], "segments": plan.num_segments,
+                "class_split": bool(plan.class_split), "stream_k": bool(plan.stream_k),
+                "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+                "dense_equivalent_flops": work["dense_flops"]}
+
+    def dtype(self):
+        return {0: "bf16", 1: "f16"}[self.w.q_dtype] + ("+fp8kv" if self.w.kv_dtype == 2 else "")
+
+    def close(self):
+        self.ua.close()
+        del self.batch
+        self.torch.cuda.empty_cache()
+
+
+def clocks_under(runner, seconds, ms_per_step, flush=None):
+    """GPU clocks during an untimed replay of the step: the firmware's table
+    refreshes too slowly to be read inside a short timed region."""
+    if seconds <= 0:
+        return None
+    clocks = ClockSampler()
+    if clocks.handle is not None:
+        reps = int(min(50000, max(1, seconds * 1e3 / max(ms_per_step, 1e-3))))
+        clocks.start()
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            runner.step()
+        runner.torch.cuda.synchronize()
+    info = clocks.stop()
+    info["replay"] = f"untimed replay of the step for about {seconds:g} s"
+    return info
+
+
+def cpu_object(w, bound, unit, budget_s, by_rows):
+    print(f"[bench] oracle CPU baseline on {w.name} (~{budget_s:.0f} s)", file=sys.stderr,
+          flush=True)
+    if by_rows:
+        c = cpu_baseline_rows(w, budget_s)
+        sample = (f"{c['rows']} seeded random (token, head) rows of the batch, "
+                  f"{c['seconds']:.1f} s of fp64 oracle time on {c['cores']} threads")
+    else:
+        c = cpu_baseline(w, budget_s)
+        sample = (f"{c['seqs']} sequence runs over {c['passes']} pass(es) of the "
+                  f"{w.num_seqs}-sequence batch (all rows and heads of each), "
+                  f"{c['seconds']:.1f} s of fp64 oracle time on {c['cores']} threads")
+    value = (c["bytes"] / c["seconds"] / 1e9) if bound == "hbm" else \
+        (c["flops"] / c["seconds"] / 1e12)
+    return {"value": round(value, 6), "unit": unit, "cores": c["cores"], "kind": "oracle",
+            "sample": sample}
+
+
+def make_read_flush(torch, nbytes=1 << 30):
+    """A cache flush that only reads: the sum of a `nbytes` buffer (larger
+    than L2 plus the 256 MiB MALL) into one value, so no dirty lines are left
+    to write back during the next timed step."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def flush():
+        torch.sum(buf, dim=0, out=sink)
+    return flush
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,9 +501,13 @@ def main():
                              "d256_prefill"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
     ap.add_argument("--cold", action="store_true",
-                    help="write a 512 MiB scratch buffer between timed steps (outside the "
-                         "events) so no step finds K/V in L2 or the MALL; value then comes "
-                         "from the summed step events instead of the wall clock")
+                    help="time the main workload cold: a read-only 1 GiB flush before every "
+                         "step (outside the events) so no step finds K/V in L2 or the MALL; "
+                         "value then comes from the summed step events")
+    ap.add_argument("--extras", default="auto",
+                    help="comma list of extra figures added to the line: 'cold' (the main "
+                         "workload again, cold) and 'prefill' (long_prefill, the MFMA-bound "
+                         "half of the metric); 'auto' = both for the decode batch, 'none'")
     ap.add_argument("--event-every", type=int, default=4,
                     help="record the kernel-timing events on every N-th timed step (warm runs)")
     ap.add_argument("--segment-tiles", type=int, default=0,
@@ -310,6 +517,8 @@ def main():
                          "samples the GPU clocks (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--prefill-cpu-seconds", type=float, default=10.0,
+                    help="wall-time budget of the prefill figure's oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (5 launches): the "
                          "reference dispatch for scaling HBM traffic counters")
@@ -330,9 +539,6 @@ def main():
         sys.exit(2)
 
     import torch
-    from varlen_attention_serving_amd import binding as B
-    from varlen_attention_serving_amd import device as D
-    from varlen_attention_serving_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -350,109 +556,41 @@ def main():
                           "launches": 5}))
         return
 
-    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
-    w = W.named(args.workload)
-    extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[args.force]
-    batch = D.DeviceBatch(w)
-    ua = D.UnifiedAttention(D.problem_desc(w, extra, split_segment_tiles=args.segment_tiles))
-    plan = ua.plan(w)
-    work = algorithmic_work(w)
-    t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = work["flops"] / (BF16_PEAK_TFLOPS * 1e12)
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    stream = torch.cuda.current_stream()
-    handle = ua.handle
-    run_args = batch.run_args(ua.workspace)
+    extras = set()
+    if args.extras == "auto":
+        if args.workload == "decode_batch" and args.force == "auto" and not args.cold:
+            extras = {"cold", "prefill"}
+    elif args.extras != "none":
+        extras = {e.strip() for e in args.extras.split(",") if e.strip()}
+        unknown = extras - {"cold", "prefill"}
+        if unknown:
+            ap.error(f"unknown extras {sorted(unknown)}")
 
-    print(f"[bench] plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
-          f"segments={plan.num_segments} grid={list(plan.grid)}; warmup {args.warmup}",
-          file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        B.ua_run(handle, run_args, stream.cuda_stream)
-    torch.cuda.synchronize()
-
-    # Events around the kernels of sampled timed steps (every step when cold).
-    # Recording them costs GPU time (about 10 us per step on decode_batch), so
-    # warm runs time the kernels on every `event_every`-th step only and leave
-    # the other steps as the workload runs in service.
-    every = 1 if args.cold else max(1, args.event_every)
-    sampled = list(range(0, args.steps, every))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
-    for trio in evs.values():
-        for e in trio:
-            e.record(stream)
-    torch.cuda.synchronize()
-
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold else None
-    print(f"[bench] timing {args.steps} steps{' (cold)' if args.cold else ''}", file=sys.stderr,
-          flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 255)
-        for j in range(3):
-            run_args.timing_events[j] = evs[i][j].cuda_event if i in evs else None
-        B.ua_run(handle, run_args, stream.cuda_stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    attn_each = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])
-    step_each = np.array([evs[i][0].elapsed_time(evs[i][2]) for i in sampled])
-    attn_ms = float(np.mean(attn_each))
-    step_gpu_ms = float(np.mean(step_each))
+    r = Runner(args.workload, args.force, args.segment_tiles)
+    flush = make_read_flush(torch) if (args.cold or "cold" in extras) else None
+    t = r.time(args.steps, args.warmup, args.event_every, flush if args.cold else None)
+    f = r.figures(t)
     # warm: whole-job wall clock over the K steps; cold: the steps' own GPU time
-    ms_per_step = step_gpu_ms if args.cold else wall * 1e3 / args.steps
+    ms_per_step = f["whole_ms"] if args.cold else t["wall_ms"]
+    value = f["value_events"] if args.cold else f["value_wall"]
+    clock_info = clocks_under(r, args.clock_seconds, ms_per_step, flush if args.cold else None)
 
-    if bound == "hbm":
-        value = work["bytes"] / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        kernel_units = work["bytes"] - (work["o_bytes"] if plan.path == 3 else 0)
-        achieved = kernel_units / (attn_ms * 1e-3) / 1e9
-        peak = HBM_PEAK_GBS
-        r_unit = "GB/s"
-    else:
-        value = work["flops"] / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        kernel_units = work["flops"]
-        achieved = kernel_units / (attn_ms * 1e-3) / 1e12
-        peak = BF16_PEAK_TFLOPS
-        r_unit = "TFLOP/s"
-    traffic = load_traffic(args.workload, plan.path)
-
-    # Clocks under this load: the firmware's table refreshes too slowly to be
-    # read inside a short timed region, so sample it over an untimed replay of
-    # the same step after the timing.
-    clock_info = None
-    if args.clock_seconds > 0:
-        clocks = ClockSampler()
-        if clocks.handle is not None:
-            reps = int(min(50000, max(1, args.clock_seconds * 1e3 / max(ms_per_step, 1e-3))))
-            clocks.start()
-            for i in range(reps):
-                B.ua_run(handle, run_args, stream.cuda_stream)
-                if flush is not None:
-                    flush.fill_(i & 0xFF)
-            torch.cuda.synchronize()
-        clock_info = clocks.stop()
-        clock_info["replay"] = f"untimed replay of the step for about {args.clock_seconds:g} s"
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        print(f"[bench] oracle CPU baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr,
-              flush=True)
-        c = cpu_baseline(w, args.cpu_seconds)
-        cpu_value = (c["bytes"] / c["seconds"] / 1e9) if bound == "hbm" else \
-            (c["flops"] / c["seconds"] / 1e12)
-        cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": c["cores"], "kind": "oracle",
-               "sample": f"{c['seqs']} sequence runs over {c['passes']} pass(es) of the "
-                         f"{w.num_seqs}-sequence batch (all rows and heads of each), "
-                         f"{c['seconds']:.1f} s of fp64 oracle time on {c['cores']} threads"}
-
-    dtype = {0: "bf16", 1: "f16"}[w.q_dtype] + ("+fp8kv" if w.kv_dtype == 2 else "")
+    config = r.config()
+    config.update({
+        "gpu_ms_per_step_events": round(f["whole_ms"], 5),
+        "attention_kernel_ms": round(f["attn_ms"], 5),
+        "timed_steps_with_events": t["sampled"],
+        "attention_kernel_ms_median": round(float(np.median(t["attn"])), 5),
+        "attention_kernel_ms_min": round(float(np.min(t["attn"])), 5),
+        "cache": "cold (read-only 1 GiB flush before each step)" if args.cold else "warm",
+        "roofline_frac_whole_step": round(max(r.t_hbm, r.t_mfma) / (ms_per_step * 1e-3), 4),
+        "roofline_frac_whole_forward_events": round(f["frac_whole_forward"], 4),
+        "clocks": clock_info,
+    })
     out = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": unit,
+        "unit": f["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -460,30 +598,54 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": r.dtype(),
         "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
-        "config": {
-            "workload": args.workload,
-            "num_seqs": w.num_seqs, "total_q": w.total_q, "max_seqlen_k": w.max_seqlen_k,
-            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim, "block_size": w.block_size,
-            "kv_layout": "dense (cu_seqlens_k)" if w.dense else "paged (block table)",
-            "path": {2: "2d", 3: "3d-split-kv"}[plan.path], "segments": plan.num_segments,
-            "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
-            "dense_equivalent_flops": work["dense_flops"],
-            "gpu_ms_per_step_events": round(step_gpu_ms, 5),
-            "attention_kernel_ms": round(attn_ms, 5),
-            "timed_steps_with_events": len(sampled),
-            "attention_kernel_ms_median": round(float(np.median(attn_each)), 5),
-            "attention_kernel_ms_min": round(float(np.min(attn_each)), 5),
-            "cache": "cold (512 MiB flush between steps)" if args.cold else "warm",
-            "roofline_frac_whole_step": round(max(t_hbm, t_mfma) / (ms_per_step * 1e-3), 4),
-            "clocks": clock_info,
-        },
-        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": r_unit, "frac": round(achieved / peak, 4), "traffic": traffic},
-        "cpu_baseline": cpu,
+        "config": config,
+        "roofline": r.roofline(f),
+        "cpu_baseline": None,
     }
+
+    if "cold" in extras:
+        tc = r.time(args.steps, 2, 1, flush)
+        fc = r.figures(tc)
+        out["cold"] = {
+            "workload": r.name, "value": round(fc["value_events"], 3), "unit": fc["unit"],
+            "ms_per_step_events": round(fc["whole_ms"], 5),
+            "attention_kernel_ms": round(fc["attn_ms"], 5),
+            "attention_kernel_ms_median": round(float(np.median(tc["attn"])), 5),
+            "roofline": {"bound": r.bound, "achieved": round(fc["achieved"], 3),
+                         "peak": fc["peak"], "unit": fc["unit"], "frac": round(fc["frac"], 4),
+                         "scope": "the attention kernel alone"},
+            "roofline_frac_whole_forward_events": round(fc["frac_whole_forward"], 4),
+            "flush": "torch.sum over a 1 GiB buffer before each step, outside the events "
+                     "(reads only: nothing dirty is left to write back in the timed step)",
+        }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_object(r.w, r.bound, f["unit"], args.cpu_seconds,
+                                         by_rows=False)
+    r.close()
+    del flush
+
+    if "prefill" in extras:
+        rp = Runner("long_prefill")
+        tp = rp.time(args.steps, args.warmup, args.event_every)
+        fp = rp.figures(tp)
+        pre = {
+            "workload": rp.name, "value": round(fp["value_wall"], 3), "unit": fp["unit"],
+            "ms_per_step": round(tp["wall_ms"], 5), "dtype": rp.dtype(),
+            "config": rp.config(),
+            "attention_kernel_ms": round(fp["attn_ms"], 5),
+            "attention_kernel_ms_median": round(float(np.median(tp["attn"])), 5),
+            "roofline_frac_whole_step": round(max(rp.t_hbm, rp.t_mfma) / (tp["wall_ms"] * 1e-3), 4),
+            "roofline": rp.roofline(fp),
+            "cpu_baseline": None,
+        }
+        if args.prefill_cpu_seconds > 0:
+            pre["cpu_baseline"] = cpu_object(rp.w, rp.bound, fp["unit"],
+                                             args.prefill_cpu_seconds, by_rows=True)
+        rp.close()
+        out["prefill"] = pre
+
     print(json.dumps(out), flush=True)
 
 

@@ -84,6 +84,11 @@ typedef struct ua_problem_desc {
     int32_t max_seqlen_k;        /* upper bound for any S_k (sizes the split workspace) */
     int32_t split_segment_tiles; /* 0 = automatic; else KV tiles per split-KV segment
                                     (>= 1; a tuning override of the plan) */
+    int32_t num_cus;             /* compute units the shape rule sizes for (its thresholds
+                                    are workgroups per CU, section 6).  0 = automatic:
+                                    ua_run queries the current device once per device;
+                                    ua_query_plan, which touches no device, assumes the
+                                    MI355X's 256.  >= 0. */
 } ua_problem_desc_t;
 
 typedef struct ua_problem* ua_problem_t;
@@ -188,20 +193,35 @@ typedef struct ua_plan_info {
 } ua_plan_info_t;
 
 /* Validate a description and build a problem handle (host only; no device
- * access).  Returns UA_ERR_INVALID_ARG / UA_ERR_UNSUPPORTED with a message. */
+ * access).  The description carries section 1's per-flag fields of the
+ * unified page (one problem object whose flags select the bias and mask
+ * steps) and the section 0 layout parameters.  `out` receives a handle the
+ * caller releases with ua_destroy_problem; on failure it is set to NULL and
+ * UA_ERR_INVALID_ARG (a field out of range) or UA_ERR_UNSUPPORTED (valid but
+ * not built, e.g. head_dim 96) is returned with a message. */
 ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out);
 
-/* Bytes of device workspace ua_run needs at the description's maxima (the
- * split-KV partials of section 5 of the unified page: fp32 o, m and l per
- * query row, head and segment).  0 for a NULL handle. */
+/* Bytes of device workspace ua_run needs at the description's maxima: the
+ * split-KV partials of section 5 of the unified page (un-normalised o, the
+ * running max m and the denominator l per query row, head and segment, plus
+ * the stream-K slots).  The caller allocates and owns it; ua_run only
+ * borrows it for the duration of the enqueued work.  0 for a NULL handle. */
 size_t ua_workspace_size(ua_problem_t problem);
 
-/* The plan ua_run would launch for these host-side shape values (host only). */
+/* The plan ua_run would launch for these host-side shape values: section 6 of
+ * the unified page's choice between the 2D query-tile kernel and the 3D
+ * split-KV kernel, with its geometry (host only; planned for
+ * desc.num_cus, or 256 compute units when that is 0).  Returns
+ * UA_ERR_INVALID_ARG when a shape exceeds the problem's maxima. */
 ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_q,
                           int32_t max_seqlen_q, int32_t max_seqlen_k, ua_plan_info_t* info);
 
-/* Enqueue one forward pass on `stream` (asynchronous; nothing is read back to
- * the host).  Validation errors return before anything is enqueued.  A
+/* Enqueue one forward pass on `stream`: section 1's operation of the unified
+ * page for every row of the batch, by the strategy of sections 4-6
+ * (asynchronous; nothing is read back to the host).  Arguments are described
+ * at ua_run_args_t; the caller keeps every buffer alive until the stream has
+ * run the work.  Validation errors (UA_ERR_INVALID_ARG, UA_ERR_WORKSPACE)
+ * return before anything is enqueued; UA_ERR_HIP reports a failed launch.  A
  * class-split run forks its stream-K launch onto a stream the handle owns
  * (created, at default priority, on the first such run; the handle then stays
  * on that device) and joins it back into `stream` before returning, so work
@@ -209,13 +229,17 @@ ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_
  * host thread at a time. */
 ua_status_t ua_run(ua_problem_t problem, const ua_run_args_t* args, void* stream);
 
-/* Release a handle (NULL is ignored). */
+/* Release a handle made by ua_create_problem (NULL is ignored).  Work already
+ * enqueued with it must have completed (it may own a side stream). */
 void ua_destroy_problem(ua_problem_t problem);
 
-/* Thread-local text of the last failure in this thread ("" if none). */
+/* Thread-local text of the last failure in this thread ("" if none): the
+ * reason a validation step rejected its input, in the manner of the dense
+ * prefill page's argument checks.  The string stays valid until the thread's
+ * next call into the library. */
 const char* ua_last_error(void);
 
-/* Library version, "major.minor.patch". */
+/* Library version, "major.minor.patch" (a static string). */
 const char* ua_version(void);
 
 #ifdef __cplusplus

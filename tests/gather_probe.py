@@ -1,6 +1,7 @@
-"""Build and call the test-only gather probe (tests/gather_probe.hip): the
-kernels' own K/V tile gathers, with each gathered LDS tile copied out densely
-so a test can compare it bit for bit with a host gather."""
+"""Build and call the test-only probe library (tests/gather_probe.hip): the
+kernels' own K/V tile gathers, with each gathered tile copied out densely so
+a test can compare it bit for bit with a host gather; the transposing LDS
+read's lane map; the kernels' fp8 conversion of every e4m3 code."""
 import ctypes
 import os
 import subprocess
@@ -11,7 +12,7 @@ SRC = os.path.join(HERE, "gather_probe.hip")
 LIB = os.path.join(HERE, "libua_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-RING, REGISTERS = 0, 1
+RING, REGISTERS, LOADER16 = 0, 1, 2
 TO_16BIT, FP8_TO_BF16, FP8_TO_F16 = 0, 1, 2
 
 
@@ -44,6 +45,10 @@ def lib():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        _lib.uap_read_tr.restype = ctypes.c_int
+        _lib.uap_read_tr.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        _lib.uap_fp8_codes.restype = ctypes.c_int
+        _lib.uap_fp8_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return _lib
 
 
@@ -65,3 +70,30 @@ def gather(batch, tiles, path, waves=4, fp8_to=TO_16BIT):
         raise RuntimeError(f"uap_gather returned {rc}")
     torch.cuda.synchronize()
     return out_k, out_v
+
+
+def read_tr(addr):
+    """One wave's ds_read_b64_tr_b16 over an LDS image whose element x holds x:
+    lane l reads at element offset addr[l] (int32 [64] device tensor,
+    multiples of 4 below 4093); returns uint16 numpy [64, 4] of what each lane
+    received."""
+    import torch
+    out = torch.zeros((64, 4), dtype=torch.int16, device=addr.device)
+    rc = lib().uap_read_tr(addr.data_ptr(), out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"uap_read_tr returned {rc}")
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view("uint16")
+
+
+def fp8_codes():
+    """The 256 e4m3 codes through the kernels' conversion: uint16 numpy [256]
+    bf16 bits and [256] f16 bits, in code order."""
+    import torch
+    ob = torch.zeros(256, dtype=torch.int16, device="cuda")
+    oh = torch.zeros_like(ob)
+    rc = lib().uap_fp8_codes(ob.data_ptr(), oh.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"uap_fp8_codes returned {rc}")
+    torch.cuda.synchronize()
+    return ob.cpu().numpy().view("uint16"), oh.cpu().numpy().view("uint16")

@@ -297,3 +297,29 @@ def test_i64_addressing_reported_above_2gib():
     p = B.ua_query_plan(h, 2, 8, 4, 512)
     assert p.use_i64_kv == 1
     B.ua_destroy_problem(h)
+
+
+def test_shape_rule_scales_with_the_compute_units():
+    """[UA] section 6 states the 2D threshold in workgroups per compute unit
+    (4 per CU): a part with half the CUs takes the 2D path for the decode
+    batch's 640-workgroup grid, the full MI355X (256 CUs, the default when
+    no device is queried) splits it."""
+    plan, _ = _named_plan("decode_batch")
+    assert plan.path == 3
+    h = B.ua_create_problem(_desc(num_q_heads=32, num_kv_heads=8, num_blocks=20000,
+                                  max_num_seqs=64, max_blocks_per_seq=512, max_total_q=64,
+                                  max_seqlen_k=8192, num_cus=128))
+    try:
+        assert B.ua_query_plan(h, 64, 64, 1, 8138).path == 2
+    finally:
+        B.ua_destroy_problem(h)
+    h = B.ua_create_problem(_desc(num_q_heads=32, num_kv_heads=8, num_blocks=20000,
+                                  max_num_seqs=64, max_blocks_per_seq=512, max_total_q=64,
+                                  max_seqlen_k=8192, num_cus=256))
+    try:
+        assert B.ua_query_plan(h, 64, 64, 1, 8138).path == 3
+    finally:
+        B.ua_destroy_problem(h)
+    with pytest.raises(B.UaError) as e:
+        B.ua_create_problem(_desc(num_cus=-1))
+    assert "num_cus" in B.ua_last_error()

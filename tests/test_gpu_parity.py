@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import compare, compare_rows, run_hip, sample_rows, say
+from gpu_common import compare, compare_rows, full_rows, run_hip, say
 from varlen_attention_serving_amd import binding as B
 from varlen_attention_serving_amd import device as D
 from varlen_attention_serving_amd import workloads as W
@@ -488,22 +488,105 @@ def test_nan_poison_in_unused_blocks_and_tails_never_reaches_output():
 
 
 # ---------------------------------------------------------------------------
-# the five named workloads at full size (sampled rows)
+# GQA groups outside the powers of two, and the widest groups
+# ---------------------------------------------------------------------------
+
+GQA_SHAPES = [
+    # (H_q, H_k, d, b, workload flags).  Groups that do not divide a q-block's
+    # rows leave rows_used < block_m on every geometry (128 / g and 32 / g
+    # positions, 16 / g on the 16-row engine); above 32 no single-wave
+    # q-block exists and stream-K is off.
+    (24, 8, 128, 16, dict()),                                   # g = 3
+    (10, 2, 64, 32, dict(use_sinks=True)),                      # g = 5
+    (12, 2, 256, 64, dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3, use_alibi=True,
+                          use_sinks=True, window=300)),          # g = 6, class split
+    (28, 4, 128, 16, dict(softcap=30.0)),                       # g = 7
+    (24, 2, 256, 32, dict(window=200, use_sinks=True)),         # g = 12, 16-row engine
+    (48, 2, 128, 16, dict(kv_dtype=W.DT_FP8_E4M3)),             # g = 24, class split
+    (64, 2, 64, 16, dict(use_alibi=True)),                      # g = 32
+    (64, 1, 128, 16, dict(use_sinks=True)),                     # g = 64
+    (128, 1, 128, 64, dict()),                                  # g = 128
+    (128, 2, 256, 64, dict(kv_dtype=W.DT_FP8_E4M3, window=250)),  # g = 64, d = 256 fp8
+]
+
+
+def _gqa_batch(i, kind):
+    """kind "mixed": decode rows, short chunks that fit a single-wave q-block
+    and longer chunks / prefill in one ragged batch; kind "decode": single
+    query rows over contexts up to 1500 keys with empty sequences."""
+    hq, hk, d, b, flags = GQA_SHAPES[i]
+    g = hq // hk
+    seed = 1200 + 10 * i + (kind == "decode")
+    rng = np.random.default_rng(seed)
+    if kind == "decode":
+        sk = rng.integers(1, 1500, size=20, endpoint=True)
+        sk[::6] = 0
+        ql = np.minimum(sk, 1)
+    else:
+        dec_k = rng.integers(1, 700, size=6, endpoint=True)
+        sq = rng.integers(2, max(2, 32 // g), size=3, endpoint=True)
+        sh_k = sq + rng.integers(0, 400, size=3, endpoint=True)
+        lq = rng.integers(30, 120, size=3, endpoint=True)
+        lk = lq + rng.integers(0, 200, size=3, endpoint=True)
+        ql = np.concatenate([np.ones(6, np.int64), sq, lq])
+        sk = np.concatenate([dec_k, sh_k, lk])
+        order = rng.permutation(ql.size)
+        ql, sk = ql[order], sk[order]
+    return W.build(f"gqa{g}_{kind}", seed, ql, sk, num_q_heads=hq, num_kv_heads=hk,
+                   head_dim=d, block_size=b, rng=rng, **flags)
+
+
+@pytest.mark.parametrize("force", ["auto", "2d", "3d", "3d_seg"])
+@pytest.mark.parametrize("i", range(len(GQA_SHAPES)))
+def test_gqa_groups_mixed_batch(i, force):
+    """[UA] section 0 (g = H_q / H_k) and section 4 (rows are (position, head)
+    pairs of one GQA group) for groups 3 to 128: every path against the oracle
+    on a batch of decode rows, short chunks and prefill rows."""
+    w = _gqa_batch(i, "mixed")
+    _, plan = _full_check(w, force, f"gqa g={w.group} d={w.head_dim} mixed/{force}")
+    if force == "auto" and w.group in (6, 12, 24):
+        assert plan.class_split == 1  # decode rows on stream-K beside the wide launch
+
+
+@pytest.mark.parametrize("force", ["auto", "3d", "3d_seg"])
+@pytest.mark.parametrize("i", range(len(GQA_SHAPES)))
+def test_gqa_groups_decode_batch(i, force):
+    """The same groups on decode-shaped batches: stream-K on the 32-row engine
+    (g <= 32), on the 16-row engine at d = 256 (g <= 16), the segmented split
+    and, above g = 32, the four-wave geometry with one or two positions per
+    q-block."""
+    w = _gqa_batch(i, "decode")
+    _, plan = _full_check(w, force, f"gqa g={w.group} d={w.head_dim} decode/{force}")
+    if force == "3d":
+        assert plan.stream_k == (1 if w.group <= 32 else 0)
+        if w.head_dim == 256 and w.group <= 16:
+            assert plan.block_m == 16
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["decode_batch", "chunked_prefill_mix", "long_prefill",
                                   "variant_mix", "dense_prefill", "mha_prefill",
                                   "d256_prefill"])
 def test_named_workload_full_size(name):
+    """The benchmark's launch configuration at full size.  O starts as NaN and
+    must come back finite everywhere (run_hip); every (token, head) row of the
+    decode-shaped sequences and every token of the others (against every kv
+    head the oracle budget allows, the query head rotating through the group)
+    is compared with the oracle."""
     say(f"[gpu] {name}: generating")
     w = W.NAMED[name]()
     batch = D.DeviceBatch(w)
     ua = D.UnifiedAttention(D.problem_desc(w))
     o, plan = run_hip(w, batch=batch, ua=ua)
-    say(f"  plan path={plan.path} waves={plan.waves} tile_n={plan.tile_n} "
-        f"segments={plan.num_segments} tps={plan.tiles_per_segment} grid={list(plan.grid)}")
-    rows = sample_rows(w, n_random=384)
-    compare_rows(o, w, rows, f"{name} ({rows.size} sampled rows)")
+    say(f"  plan path={plan.path} split={plan.class_split} stream_k={plan.stream_k} "
+        f"waves={plan.waves} tile_n={plan.tile_n} segments={plan.num_segments} "
+        f"tps={plan.tiles_per_segment} grid={list(plan.grid)}")
+    rows, m = full_rows(w)
+    say(f"  comparing {rows.size} rows ({m} of {w.num_kv_heads} kv heads per prefill token)")
+    compare_rows(o, w, rows, f"{name} ({rows.size} rows)")
     # a second run in the same configuration is bitwise identical
     o2, _ = run_hip(w, batch=batch, ua=ua)
     assert np.array_equal(o, o2)

@@ -59,6 +59,7 @@ class ua_problem_desc_t(ctypes.Structure):
         ("max_total_q", ctypes.c_int64),
         ("max_seqlen_k", ctypes.c_int32),
         ("split_segment_tiles", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
     ]
 
 

@@ -14,17 +14,20 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "ua.h"
 #include "ua_internal.h"
 
 namespace {
 
-constexpr int kNumCUs = 256;            // MI355X compute units
+constexpr int kDefaultCUs = 256;        // MI355X compute units (plans made without a device)
 constexpr int kMinTilesPerSegment = 4;  // keep each split segment worth its partials
-constexpr int kSplitTargetWorkgroups = 8 * kNumCUs;
+constexpr int kSplitWorkgroupsPerCU = 8;
 constexpr int kWideResidentPerCU = 3;   // four-wave workgroups resident per CU
 constexpr int kMaxWideSegments = 2;
 constexpr size_t kWorkspaceCap = size_t(2) << 30;
@@ -121,21 +124,21 @@ void rows16(const ua_problem& P, Sub* g) {
 // The segmented split: grid z holds the segments; each q-block cuts its own
 // live tile range into up to that many near-equal runs of about
 // tiles_per_seg tiles (the kernel and the reduce agree on the cut).
-ua_status_t segmented(const ua_problem& P, int64_t total_q, int64_t live_blocks, int64_t span,
-                      size_t ws_cap, Sub* g) {
+ua_status_t segmented(const ua_problem& P, int cus, int64_t total_q, int64_t live_blocks,
+                      int64_t span, size_t ws_cap, Sub* g) {
     const ua_problem_desc_t& d = P.d;
     g->path = 3;
     const int64_t max_tiles = std::max<int64_t>(1, cdiv(std::max<int64_t>(span, 1), g->tile_n) + 1);
     // expected live tiles (ragged lengths: about half of the maximum) over
     // the workgroups we want resident
     const int64_t work = std::max<int64_t>(1, d.num_kv_heads * live_blocks * max_tiles / 2);
-    int64_t tps = std::max<int64_t>(kMinTilesPerSegment, cdiv(work, kSplitTargetWorkgroups));
+    int64_t tps = std::max<int64_t>(kMinTilesPerSegment, cdiv(work, (int64_t)kSplitWorkgroupsPerCU * cus));
     int64_t ns = 0;
     if (g->waves > 1 && d.split_segment_tiles == 0) {
         // about two resident rounds of wide workgroups: each q-block cuts its
         // own tile range into up to ns runs of at least kMinTilesPerSegment
         const int64_t grid = std::max<int64_t>(1, d.num_kv_heads * (total_q / g->block_q + 1));
-        ns = std::min<int64_t>(kMaxWideSegments, cdiv(2 * kWideResidentPerCU * kNumCUs, grid));
+        ns = std::min<int64_t>(kMaxWideSegments, cdiv((int64_t)2 * kWideResidentPerCU * cus, grid));
         tps = kMinTilesPerSegment;
         ns = std::max<int64_t>(1, std::min(ns, cdiv(max_tiles, tps)));
     } else {
@@ -158,8 +161,8 @@ ua_status_t segmented(const ua_problem& P, int64_t total_q, int64_t live_blocks,
     return UA_OK;
 }
 
-ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, int32_t max_q,
-                      int32_t max_k, Plan* out) {
+ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t total_q,
+                      int32_t max_q, int32_t max_k, Plan* out) {
     const ua_problem_desc_t& d = P.d;
     Plan pl{};
     pl.small_block_q = use_rows16(P) ? 16 / P.group : P.group <= 32 ? 32 / P.group : 0;
@@ -184,13 +187,13 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
     if (w.slots > INT32_MAX / 2) return fail(UA_ERR_UNSUPPORTED, "too many query blocks");
     // q-blocks that carry rows (at most one partial block per sequence)
     const int64_t live_blocks = std::min<int64_t>(w.slots, num_seqs + total_q / w.block_q);
-    bool two_d = (int64_t)d.num_kv_heads * w.slots >= 4 * kNumCUs || span <= 512;
+    bool two_d = (int64_t)d.num_kv_heads * w.slots >= (int64_t)4 * cus || span <= 512;
     if (!small && !two_d) {
         // Wide q-blocks carry 128 fp32 rows of partials per segment, so split
         // them only when the query-tile grid is short of one resident round
         // (three four-wave workgroups per CU), and only as far as needed.
         const int64_t wide_grid = (int64_t)d.num_kv_heads * (total_q / w.block_q + 1);
-        two_d = wide_grid >= kWideResidentPerCU * kNumCUs;
+        two_d = wide_grid >= (int64_t)kWideResidentPerCU * cus;
     }
     // Wide q-blocks of 16-bit K/V run on the LDS ring (at d = 256 only
     // without score transforms; blocks must hold one copy's 512 / d key
@@ -202,7 +205,7 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
                       (int64_t(1) << P.log2_block) * d.head_dim >= 512 &&
                       (int64_t)d.num_kv_heads * d.head_dim * 2 * (512 / d.head_dim) < (int64_t(1) << 31);
     const bool ring_fills =
-        !small && ring && (int64_t)d.num_kv_heads * w.slots >= kWideResidentPerCU * kNumCUs;
+        !small && ring && (int64_t)d.num_kv_heads * w.slots >= (int64_t)kWideResidentPerCU * cus;
     if (ring_fills) two_d = true;
     if (force2) two_d = true;
     if (force3) two_d = false;
@@ -259,11 +262,37 @@ ua_status_t make_plan(const ua_problem& P, int32_t num_seqs, int64_t total_q, in
         if (stream_k_bytes(P, num_seqs, g.block_q * P.group) > P.ws_bytes)
             return fail(UA_ERR_WORKSPACE, "workspace too small for the split path");
     } else {
-        ua_status_t st = segmented(P, total_q, live_blocks, span, ws_seg, &g);
+        ua_status_t st = segmented(P, cus, total_q, live_blocks, span, ws_seg, &g);
         if (st != UA_OK) return st;
     }
     *out = pl;
     return UA_OK;
+}
+
+// Compute units of the current device, queried once per device (the plan's
+// thresholds are in workgroups per compute unit).  0 when no device answers.
+int device_cus() {
+    static std::mutex mu;
+    static std::vector<std::pair<int, int>> cache;  // (device, CUs)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+        if (e.first == dev) return e.second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return 0;
+    cache.push_back({dev, cus});
+    return cus;
+}
+
+// The compute units a plan is sized for: the descriptor's count, else (on the
+// run path) the device's, else the MI355X's 256.
+int plan_cus(const ua_problem& P, bool on_device) {
+    if (P.d.num_cus > 0) return P.d.num_cus;
+    const int c = on_device ? device_cus() : 0;
+    return c > 0 ? c : kDefaultCUs;
 }
 
 }  // namespace
@@ -320,6 +349,7 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     if (d.max_total_q > INT32_MAX) return fail(UA_ERR_UNSUPPORTED, "max_total_q exceeds 2^31");
     if (d.split_segment_tiles < 0)
         return fail(UA_ERR_INVALID_ARG, "split_segment_tiles must be >= 0");
+    if (d.num_cus < 0) return fail(UA_ERR_INVALID_ARG, "num_cus must be >= 0");
     const bool dense = (d.flags & UA_FLAG_DENSE_KV) != 0;
     if (dense && d.block_size != 1)
         return fail(UA_ERR_INVALID_ARG, "the dense K/V layout needs block_size 1 (got %d)",
@@ -368,7 +398,8 @@ ua_status_t ua_query_plan(ua_problem_t p, int32_t num_seqs, int64_t total_q, int
         max_seqlen_q < 0 || max_seqlen_q > max_seqlen_k)
         return fail(UA_ERR_INVALID_ARG, "shape outside the problem's maxima");
     Plan pl;
-    ua_status_t st = make_plan(*p, num_seqs, total_q, max_seqlen_q, max_seqlen_k, &pl);
+    ua_status_t st = make_plan(*p, plan_cus(*p, false), num_seqs, total_q, max_seqlen_q,
+                               max_seqlen_k, &pl);
     if (st != UA_OK) return st;
     const Sub& g = pl.sub[pl.n - 1];  // the launch holding the widest rows
     info->path = g.path;
@@ -437,7 +468,8 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     }
 
     Plan pl;
-    ua_status_t st = make_plan(*p, a->num_seqs, a->total_q, a->max_seqlen_q, a->max_seqlen_k, &pl);
+    ua_status_t st = make_plan(*p, plan_cus(*p, true), a->num_seqs, a->total_q, a->max_seqlen_q,
+                               a->max_seqlen_k, &pl);
     if (st != UA_OK) return st;
 
     UaKernelParams base{};
