@@ -229,6 +229,23 @@ ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_
  * host thread at a time. */
 ua_status_t ua_run(ua_problem_t problem, const ua_run_args_t* args, void* stream);
 
+/* ua_run for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * plan and kernels as ua_run, but the split-KV partials live in a scratch
+ * array the library holds on each GPU it runs on (128 MiB, kept until the
+ * process ends), so `workspace` must be NULL and `workspace_bytes` 0
+ * (UA_ERR_INVALID_ARG otherwise).  Nothing is allocated or freed: a batch
+ * whose partials do not fit returns UA_ERR_WORKSPACE before anything is
+ * enqueued (the stream-K workers are capped to the slots the scratch holds;
+ * a segmented split must fit whole).  A class-split batch runs its two
+ * launches one after the other on `stream` instead of forking a side stream.
+ * No part of the scratch needs to start at zero: every partial the reduce
+ * reads is written earlier by the same call.  Calls on one GPU share its
+ * scratch, so calls whose work overlaps on that GPU (other streams, other
+ * threads) race: serialise them.  The first call on a device looks up the
+ * scratch's device address (HIP may load the library's code object then). */
+ua_status_t ua_run_no_alloc(ua_problem_t problem, const ua_run_args_t* args, void* stream);
+
 /* Release a handle made by ua_create_problem (NULL is ignored).  Work already
  * enqueued with it must have completed (it may own a side stream). */
 void ua_destroy_problem(ua_problem_t problem);

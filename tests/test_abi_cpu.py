@@ -323,3 +323,27 @@ def test_shape_rule_scales_with_the_compute_units():
     with pytest.raises(B.UaError) as e:
         B.ua_create_problem(_desc(num_cus=-1))
     assert "num_cus" in B.ua_last_error()
+
+
+def test_no_alloc_refuses_before_touching_a_device():
+    """ua_run_no_alloc takes no workspace and refuses a batch whose split
+    partials exceed its scratch; both checks come before any device call."""
+    d = _desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_FORCE_3D, split_segment_tiles=1,
+              max_total_q=600_000)
+    h = B.ua_create_problem(d)
+    try:
+        args = B.ua_run_args_t(q=16, k_cache=16, v_cache=16, o=16 * 3, block_table=16,
+                               seq_lens=16, cu_seqlens_q=16, num_seqs=4, max_seqlen_q=60,
+                               total_q=600_000, max_seqlen_k=1000, block_table_stride=63,
+                               q_stride_tok=8 * 128, o_stride_tok=8 * 128)
+        with pytest.raises(B.UaError) as e:
+            B.ua_run_no_alloc(h, args, None)
+        assert e.value.status == B.UA_ERR_WORKSPACE
+        assert "scratch" in B.ua_last_error()
+        args.workspace = 256
+        args.workspace_bytes = 1 << 20
+        with pytest.raises(B.UaError) as e:
+            B.ua_run_no_alloc(h, args, None)
+        assert e.value.status == B.UA_ERR_INVALID_ARG
+    finally:
+        B.ua_destroy_problem(h)

@@ -36,7 +36,7 @@ STATUS_NAMES = {UA_OK: "UA_OK", UA_ERR_INVALID_ARG: "UA_ERR_INVALID_ARG",
 
 # every symbol include/ua.h declares
 EXPORTS = ("ua_create_problem", "ua_workspace_size", "ua_query_plan", "ua_run",
-           "ua_destroy_problem", "ua_last_error", "ua_version")
+           "ua_run_no_alloc", "ua_destroy_problem", "ua_last_error", "ua_version")
 
 
 class ua_problem_desc_t(ctypes.Structure):
@@ -128,6 +128,8 @@ def _load():
     L.ua_query_plan.restype = ctypes.c_int
     L.ua_run.argtypes = [vp, ctypes.POINTER(ua_run_args_t), vp]
     L.ua_run.restype = ctypes.c_int
+    L.ua_run_no_alloc.argtypes = [vp, ctypes.POINTER(ua_run_args_t), vp]
+    L.ua_run_no_alloc.restype = ctypes.c_int
     L.ua_destroy_problem.argtypes = [vp]
     L.ua_destroy_problem.restype = None
     L.ua_last_error.argtypes = []
@@ -173,6 +175,10 @@ def ua_query_plan(problem, num_seqs: int, total_q: int, max_seqlen_q: int,
 
 def ua_run(problem, args: ua_run_args_t, stream) -> None:
     _check(lib.ua_run(problem, ctypes.byref(args), stream))
+
+
+def ua_run_no_alloc(problem, args: ua_run_args_t, stream) -> None:
+    _check(lib.ua_run_no_alloc(problem, ctypes.byref(args), stream))
 
 
 def ua_destroy_problem(problem) -> None:

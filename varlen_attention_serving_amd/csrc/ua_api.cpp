@@ -91,9 +91,11 @@ struct Plan {
                        // engine, else 32 / g; 0 if g > 32)
 };
 
-// stream-K partial slots: one per (sequence, kv-head) pair plus one per worker
-size_t stream_k_bytes(const ua_problem& P, int64_t num_seqs, int rows_per_slot) {
-    const size_t b = (size_t)(num_seqs * P.d.num_kv_heads + kMaxStreamKWorkers) * rows_per_slot *
+// stream-K partial slots: one per (sequence, kv-head) pair plus one per
+// worker wave (at most `extra` of them)
+size_t stream_k_bytes(const ua_problem& P, int64_t num_seqs, int rows_per_slot,
+                      int64_t extra = kMaxStreamKWorkers) {
+    const size_t b = (size_t)(num_seqs * P.d.num_kv_heads + extra) * rows_per_slot *
                      (size_t)row_bytes(P);
     return (b + 255) & ~size_t(255);
 }
@@ -419,8 +421,46 @@ ua_status_t ua_query_plan(ua_problem_t p, int32_t num_seqs, int64_t total_q, int
     return UA_OK;
 }
 
-ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
-    g_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Scratch for callers that cannot allocate (ua_run_no_alloc): the split-KV
+// partials of a run live here instead of in a caller workspace.  Every GPU
+// the library runs on holds its own copy until the process ends; calls on
+// one GPU share it.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of this device's scratch, looked up once per device
+// (with that device current) and kept: in host code `scratch` names a host
+// stand-in, not device memory.
+ua_status_t scratch_address(void** out) {
+    static std::mutex mu;
+    static std::vector<std::pair<int, void*>> table;  // (device, address)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(UA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& t : table)
+        if (t.first == dev) {
+            *out = t.second;
+            return UA_OK;
+        }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return fail(UA_ERR_HIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+    table.push_back({dev, ptr});
+    *out = ptr;
+    return UA_OK;
+}
+
+// One forward pass.  With `no_alloc` the split partials go to this device's
+// scratch (the caller's workspace fields must be empty), the stream-K workers
+// are capped to the slots the scratch holds, and a class split runs its two
+// launches one after the other on `stream` (no side stream is created).
+ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool no_alloc) {
     if (!p || !a) return fail(UA_ERR_INVALID_ARG, "null handle or arguments");
     const ua_problem_desc_t& d = p->d;
     if (a->num_seqs < 0 || a->num_seqs > d.max_num_seqs)
@@ -507,26 +547,61 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     base.sk_heads = 1;
 
     // workspace: [segmented partials][stream-K partials], both 256-byte aligned
+    if (no_alloc && (a->workspace || a->workspace_bytes))
+        return fail(UA_ERR_INVALID_ARG,
+                    "ua_run_no_alloc uses its own scratch: workspace must be NULL and 0 bytes");
     if (a->workspace && ((uintptr_t)a->workspace & 255))
         return fail(UA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     size_t need = 0;
     size_t seg_bytes = 0, sk_bytes = 0;
+    int64_t sk_extra = kMaxStreamKWorkers;  // stream-K slots beyond one per (seq, kv head)
+    int sk_rows = 0;
     for (int i = 0; i < pl.n; ++i) {
         const Sub& g = pl.sub[i];
         if (g.path == 3 && g.stream_k)
-            sk_bytes = stream_k_bytes(*p, a->num_seqs, g.block_q * p->group);
+            sk_rows = g.block_q * p->group;
         else if (g.path == 3)
             seg_bytes = ((size_t)a->total_q * d.num_q_heads * g.num_segments * row_bytes(*p) + 255) &
                         ~size_t(255);
     }
+    if (no_alloc && sk_rows) {
+        // as many worker slots as the scratch holds beside the segmented
+        // region, at least one eight-wave worker, at most the usual bound
+        const size_t per_slot = (size_t)sk_rows * row_bytes(*p);
+        const int64_t fit = seg_bytes < kScratchBytes
+                                ? (int64_t)((kScratchBytes - seg_bytes - 255) / per_slot) -
+                                      (int64_t)a->num_seqs * d.num_kv_heads
+                                : 0;
+        sk_extra = std::min<int64_t>(kMaxStreamKWorkers, fit);
+        if (sk_extra < kSkMaxWorkerWaves)
+            return fail(UA_ERR_WORKSPACE,
+                        "batch too large for ua_run_no_alloc: its split partials need more than "
+                        "the %zu-byte scratch (use ua_run with a workspace)",
+                        kScratchBytes);
+    }
+    if (sk_rows) sk_bytes = stream_k_bytes(*p, a->num_seqs, sk_rows, sk_extra);
     need = seg_bytes + sk_bytes;
-    if (need && (!a->workspace || a->workspace_bytes < need))
+    void* ws_base = a->workspace;
+    if (no_alloc) {
+        if (need > kScratchBytes)
+            return fail(UA_ERR_WORKSPACE,
+                        "batch too large for ua_run_no_alloc: its split partials need %zu bytes, "
+                        "the scratch holds %zu (use ua_run with a workspace)",
+                        need, kScratchBytes);
+        if (need) {
+            ua_status_t sst = scratch_address(&ws_base);
+            if (sst != UA_OK) return sst;
+        }
+    } else if (need && (!a->workspace || a->workspace_bytes < need)) {
         return fail(UA_ERR_WORKSPACE, "split path needs %zu workspace bytes, got %zu", need,
                     a->workspace ? a->workspace_bytes : (size_t)0);
+    }
+    // a no-alloc class split runs both launches on the caller's stream
+    const bool use_side = pl.n == 2 && !no_alloc;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t* tev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(a->timing_events));
-    if (pl.n == 2) {
+    if (use_side) {
         // The two launches share no data until the output: fork the stream-K
         // (HBM-bound) launch onto the side stream so it fills the compute
         // units the wide (MFMA-bound) launch leaves free.
@@ -579,10 +654,10 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         l.rows16 = g.rows16;
         for (int j = 0; j < 3; ++j) l.grid[j] = g.grid[j];
         l.reduce_rows = a->total_q * d.num_q_heads;
+        l.sk_waves_cap = (int)sk_extra;
         if (g.path == 3 && g.stream_k) {
-            float* ws = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + seg_bytes);
-            const size_t rows =
-                ((size_t)a->num_seqs * d.num_kv_heads + kMaxStreamKWorkers) * kp.rows_used;
+            float* ws = reinterpret_cast<float*>(static_cast<char*>(ws_base) + seg_bytes);
+            const size_t rows = ((size_t)a->num_seqs * d.num_kv_heads + sk_extra) * kp.rows_used;
             kp.ws_o = ws;
             kp.ws_m = ws + rows * d.head_dim;
             kp.ws_l = kp.ws_m + rows;
@@ -593,7 +668,7 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
             if (kp.reduce_by_seq) l.reduce_rows = by_seq;
         } else if (g.path == 3) {
             const size_t rows = (size_t)a->total_q * d.num_q_heads;
-            float* ws = static_cast<float*>(a->workspace);
+            float* ws = static_cast<float*>(ws_base);
             kp.ws_o = ws;
             kp.ws_m = ws + rows * g.num_segments * d.head_dim;
             kp.ws_l = kp.ws_m + rows * g.num_segments;
@@ -602,7 +677,9 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         // it, [2] after its reduce; a split batch records its own around both
         if (pl.n == 1)
             for (int j = 0; j < 3; ++j) l.events[j] = tev[j];
-        hipStream_t st = i == 0 && pl.n == 2 ? p->side : s;
+        else if (!use_side && i == pl.n - 1)
+            l.events[0] = tev[0];
+        hipStream_t st = i == 0 && use_side ? p->side : s;
         hipError_t e;
         switch (d.head_dim) {
             case 64: e = ua_launch_d64(kp, l, st); break;
@@ -611,7 +688,12 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
         }
         if (e != hipSuccess) return fail(UA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     }
-    if (pl.n == 2) {
+    if (pl.n == 2 && !use_side) {
+        hipError_t e;
+        if ((tev[1] && (e = hipEventRecord(tev[1], s)) != hipSuccess) ||
+            (tev[2] && (e = hipEventRecord(tev[2], s)) != hipSuccess))
+            return fail(UA_ERR_HIP, "timing events: %s", hipGetErrorString(e));
+    } else if (pl.n == 2) {
         hipError_t e;
         if ((e = hipEventRecord(p->join, p->side)) != hipSuccess ||
             (e = hipStreamWaitEvent(s, p->join, 0)) != hipSuccess ||
@@ -620,6 +702,20 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
             return fail(UA_ERR_HIP, "join: %s", hipGetErrorString(e));
     }
     return UA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
+    g_error.clear();
+    return run_impl(p, a, stream, false);
+}
+
+ua_status_t ua_run_no_alloc(ua_problem_t p, const ua_run_args_t* a, void* stream) {
+    g_error.clear();
+    return run_impl(p, a, stream, true);
 }
 
 }  // extern "C"

@@ -113,6 +113,7 @@ constexpr int min_waves_per_simd(int d, int waves) {
 #define UA_SK_HEADS 8
 #endif
 constexpr int kSkMaxHeads = UA_SK_HEADS;
+static_assert(kSkMaxHeads <= kSkMaxWorkerWaves, "the workspace bound counts at most 8 waves a worker");
 
 // Score transforms a kernel is compiled for: none (the scale folds into the
 // exponent), softcap and/or ALiBi (tested per tile from the flags), or those
@@ -1974,7 +1975,7 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
                     const size_t lds = (size_t)gh * Geom16<D, FP8>::BN * Geom16<D, FP8>::VSTR * 2;
                     auto kern = p.block_size_log2 >= 4 ? ua_decode16_kernel<D, QT, FP8, XF, true>
                                                        : ua_decode16_kernel<D, QT, FP8, XF, false>;
-                    workers = std::min(resident_workgroups(kern, gh, lds), (int)kMaxStreamKWorkers / gh);
+                    workers = std::min(resident_workgroups(kern, gh, lds), l.sk_waves_cap / gh);
                     p.sk_workers = workers;
                     hipLaunchKernelGGL(kern, dim3(workers), dim3(64 * gh), lds, st, p);
                 } else {
@@ -1987,7 +1988,7 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
                 p.sk_heads = gh;
                 const size_t lds = (size_t)gh * sk_wave_lds_elems<D, BN, FP8>() * 2;
                 auto kern = ua_decode_sk_kernel<D, BN, QT, FP8, XF>;
-                workers = std::min(resident_workgroups(kern, gh, lds), (int)kMaxStreamKWorkers / gh);
+                workers = std::min(resident_workgroups(kern, gh, lds), l.sk_waves_cap / gh);
                 p.sk_workers = workers;
                 hipLaunchKernelGGL(kern, dim3(workers), dim3(64 * gh), lds, st, p);
             }

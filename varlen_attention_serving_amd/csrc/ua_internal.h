@@ -53,6 +53,8 @@ struct UaKernelParams {
 
 // Upper bound on stream-K workers (sizes the workspace before the device is known).
 constexpr int kMaxStreamKWorkers = 8192;
+// Waves of the widest stream-K worker (one per kv head of its group).
+constexpr int kSkMaxWorkerWaves = 8;
 // KV tile of the single-wave (decode) geometry, the only one the stream-K split uses.
 constexpr int kSkTile = 32;
 
@@ -68,6 +70,8 @@ struct UaLaunch {
     int rows16;      // stream-K with 16-row q-blocks (16x16x32 MFMA engine)
     int64_t reduce_rows;  // split path: total_q * H_q
     hipEvent_t events[3]; // optional: before attention, between kernels, at the end
+    int sk_waves_cap;     // stream-K: at most this many workers * waves per worker (the
+                          // workspace holds that many slots beyond one per (seq, kv head))
 };
 
 hipError_t ua_launch_d64(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
