@@ -323,7 +323,7 @@ def _visible(w, s):
 class Runner:
     """One workload on the device: its batch, problem handle and plan."""
 
-    def __init__(self, name, force="auto", segment_tiles=0):
+    def __init__(self, name, force="auto", segment_tiles=0, extra_flags=0):
         from varlen_attention_serving_amd import binding as B
         from varlen_attention_serving_amd import device as D
         from varlen_attention_serving_amd import workloads as W
@@ -332,7 +332,7 @@ class Runner:
         print(f"[bench] generating {name}", file=sys.stderr, flush=True)
         self.name = name
         self.w = w = W.named(name)
-        extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[force]
+        extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[force] | extra_flags
         self.batch = D.DeviceBatch(w)
         self.ua = D.UnifiedAttention(D.problem_desc(w, extra, split_segment_tiles=segment_tiles))
         self.plan = self.ua.plan(w)
@@ -512,6 +512,8 @@ def main():
                     help="record the kernel-timing events on every N-th timed step (warm runs)")
     ap.add_argument("--segment-tiles", type=int, default=0,
                     help="split-KV segment length in KV tiles (0 = the plan's choice)")
+    ap.add_argument("--bf16-partials", action="store_true",
+                    help="keep the split-KV partial o in bf16 (UA_FLAG_BF16_PARTIALS)")
     ap.add_argument("--clock-seconds", type=float, default=1.0,
                     help="seconds of untimed replay after timing during which amdsmi "
                          "samples the GPU clocks (0 = skip)")
@@ -566,7 +568,9 @@ def main():
         if unknown:
             ap.error(f"unknown extras {sorted(unknown)}")
 
-    r = Runner(args.workload, args.force, args.segment_tiles)
+    from varlen_attention_serving_amd import binding as B
+    r = Runner(args.workload, args.force, args.segment_tiles,
+               B.UA_FLAG_BF16_PARTIALS if args.bf16_partials else 0)
     flush = make_read_flush(torch) if (args.cold or "cold" in extras) else None
     t = r.time(args.steps, args.warmup, args.event_every, flush if args.cold else None)
     f = r.figures(t)
@@ -583,6 +587,7 @@ def main():
         "attention_kernel_ms_median": round(float(np.median(t["attn"])), 5),
         "attention_kernel_ms_min": round(float(np.min(t["attn"])), 5),
         "cache": "cold (read-only 1 GiB flush before each step)" if args.cold else "warm",
+        "split_partials": "bf16" if args.bf16_partials else "f32",
         "roofline_frac_whole_step": round(max(r.t_hbm, r.t_mfma) / (ms_per_step * 1e-3), 4),
         "roofline_frac_whole_forward_events": round(f["frac_whole_forward"], 4),
         "clocks": clock_info,

@@ -57,8 +57,19 @@ enum {
     UA_FLAG_SINKS = 1u << 4,    /* per-head logit joins the softmax with no value row */
     UA_FLAG_QQ_BIAS = 1u << 5,  /* bias[q_local][k - ctx] on keys of the query section */
     UA_FLAG_DENSE_KV = 1u << 6, /* K/V packed per sequence: rows cu_seqlens_k[s] + k */
+    UA_FLAG_BF16_PARTIALS = 1u << 7, /* split-KV partial o kept in bf16 in the workspace
+                                    (m and l stay f32): about half the partial bytes
+                                    and a smaller ua_workspace_size; each partial is
+                                    rounded to bf16 (2^-9 relative) before the merge */
     UA_FLAG_FORCE_2D = 1u << 8, /* testing/benchmarking: bypass the shape rule */
     UA_FLAG_FORCE_3D = 1u << 9
+};
+
+/* Element type of caller-held partial states (ua_run_args_t.partial_o and
+ * ua_merge_args_t). */
+enum {
+    UA_PARTIAL_F32 = 0,
+    UA_PARTIAL_BF16 = 1
 };
 
 /* Problem description: everything that fixes the kernel and the plan bounds.
@@ -145,6 +156,21 @@ typedef struct ua_problem* ua_problem_t;
  *               The denominator sums the same 16-bit-rounded p as O, so it
  *               agrees with the exact value to about 2^-9 relative (LSE to
  *               about 2e-3 absolute).  4-byte aligned.
+ *  partial_o    optional device [total_q, H_q, d] (16-byte aligned; NULL = a
+ *               normal run).  When set the run leaves its result unnormalised
+ *               across calls ("skip the final merge"): instead of O (which
+ *               may then be NULL) and `lse` it writes, per row, the
+ *               merge-ready state of the (o, m, l) recurrence over this call's
+ *               keys: o / l (times v_scale for fp8 V) here, in partial_dtype,
+ *               and ln l + m ln 2, the row's natural-log LSE, to partial_lse
+ *               (0 and -inf for a row that saw no key).  Sinks are left out,
+ *               so that ua_merge can join them exactly once.  Section 5 of the
+ *               unified page merges such states associatively; callers use
+ *               this for shared-prefix (cascade) batches and for keys split
+ *               over devices or calls.
+ *  partial_lse  device f32 [total_q, H_q], 4-byte aligned; required with partial_o.
+ *  partial_dtype  UA_PARTIAL_F32 or UA_PARTIAL_BF16 (bf16 rounds o / l to 8
+ *               significant bits; the LSE stays f32).
  * Device metadata is trusted: 0 <= q_len <= S_k <= max_seqlen_k, and used
  * block-table entries lie in [0, num_blocks). */
 typedef struct ua_run_args {
@@ -171,7 +197,37 @@ typedef struct ua_run_args {
     const float* qq_bias;
     int32_t qq_bias_stride;
     const int32_t* cu_seqlens_k;
+    void* partial_o;
+    float* partial_lse;
+    int32_t partial_dtype;
 } ua_run_args_t;
+
+/* Most partial states one ua_merge call combines. */
+#define UA_MAX_MERGE_SETS 8
+
+/* Arguments of ua_merge: num_sets partial states of the same rows, each as
+ * ua_run writes them with partial_o set (row r = token * H_q + head).
+ *  partial_o[i]    device [total_q, H_q, head_dim] in partial_dtype, 16-byte aligned
+ *  partial_lse[i]  device f32 [total_q, H_q] natural-log LSE (-inf: empty set)
+ *  sinks           optional device f32 [H_q] natural-log sink logits (NULL: none),
+ *                  joined once into every row's denominator
+ *  o               device [total_q, H_q, head_dim] in o_dtype (bf16 / f16), token
+ *                  stride o_stride_tok elements (>= H_q * head_dim, multiple of 8)
+ *  lse             optional device f32 [total_q, H_q]: the merged natural-log LSE */
+typedef struct ua_merge_args {
+    int32_t num_sets;
+    int32_t partial_dtype;
+    const void* partial_o[UA_MAX_MERGE_SETS];
+    const float* partial_lse[UA_MAX_MERGE_SETS];
+    int64_t total_q;
+    int32_t num_q_heads;
+    int32_t head_dim;
+    int32_t o_dtype;
+    int64_t o_stride_tok;
+    void* o;
+    float* lse;
+    const float* sinks;
+} ua_merge_args_t;
 
 /* Which kernel strategy a run takes (section 6 of the unified page). */
 typedef struct ua_plan_info {
@@ -228,6 +284,17 @@ ua_status_t ua_query_plan(ua_problem_t problem, int32_t num_seqs, int64_t total_
  * enqueued on `stream` afterwards sees the whole output.  A handle serves one
  * host thread at a time. */
 ua_status_t ua_run(ua_problem_t problem, const ua_run_args_t* args, void* stream);
+
+/* Combine partial states over disjoint key sets of the same rows into O (and
+ * optionally the LSE): section 5 of the unified page's log-sum-exp re-base,
+ * LSE = ln(sum_i e^{lse_i} + e^{sink}) and O = sum_i o_i e^{lse_i - LSE}, with
+ * the sink (one more softmax column without a value row, section 1) joined
+ * exactly once.  A row whose sets are all empty and that has no sink gets
+ * O = 0 and LSE = -inf.  Asynchronous on `stream`; the sets may be any of
+ * this or other calls' outputs (they are only read).  UA_ERR_INVALID_ARG for
+ * a count outside [1, UA_MAX_MERGE_SETS], a NULL or misaligned pointer, or a
+ * shape or type out of range; UA_ERR_HIP for a failed launch. */
+ua_status_t ua_merge(const ua_merge_args_t* args, void* stream);
 
 /* ua_run for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same

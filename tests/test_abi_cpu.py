@@ -347,3 +347,67 @@ def test_no_alloc_refuses_before_touching_a_device():
         assert e.value.status == B.UA_ERR_INVALID_ARG
     finally:
         B.ua_destroy_problem(h)
+
+
+def test_bf16_partials_halve_the_split_workspace():
+    """UA_FLAG_BF16_PARTIALS stores the partial o in bf16: the workspace of
+    the decode batch's segmented split (and of its stream-K slots) shrinks
+    by (2 d + 8) / (4 d + 8) = 264 / 520 at d = 128."""
+    kw = dict(num_q_heads=32, num_kv_heads=8, num_blocks=20000, max_num_seqs=64,
+              max_blocks_per_seq=512, max_total_q=64, max_seqlen_k=8192, split_segment_tiles=16)
+    sizes = []
+    for extra in (0, B.UA_FLAG_BF16_PARTIALS):
+        h = B.ua_create_problem(_desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_FORCE_3D | extra, **kw))
+        try:
+            assert B.ua_query_plan(h, 64, 64, 1, 8138).path == 3
+            sizes.append(B.ua_workspace_size(h))
+        finally:
+            B.ua_destroy_problem(h)
+    assert abs(sizes[1] / sizes[0] - 264 / 520) < 1e-3, sizes
+
+
+MERGE_BAD = [
+    (dict(num_sets=0), "num_sets"),
+    (dict(num_sets=9), "num_sets"),
+    (dict(partial_dtype=5), "partial_dtype"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(o_dtype=B.UA_DTYPE_FP8_E4M3), "o_dtype"),
+    (dict(o_stride_tok=100), "o_stride_tok"),
+    (dict(o=8), "o must be"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MERGE_BAD)))
+def test_merge_rejects_invalid_arguments(i):
+    kw, text = MERGE_BAD[i]
+    base = dict(num_sets=2, partial_dtype=B.UA_PARTIAL_F32, total_q=4, num_q_heads=8,
+                head_dim=128, o_dtype=B.UA_DTYPE_BF16, o_stride_tok=1024, o=4096)
+    base.update(kw)
+    a = B.ua_merge_args_t(**base)
+    for j in range(2):
+        a.partial_o[j] = 8192
+        a.partial_lse[j] = 8192
+    with pytest.raises(B.UaError) as e:
+        B.ua_merge(a, None)
+    assert text in B.ua_last_error()
+
+
+def test_merge_rejects_a_missing_set_and_partial_mode_needs_lse():
+    a = B.ua_merge_args_t(num_sets=2, partial_dtype=B.UA_PARTIAL_F32, total_q=4, num_q_heads=8,
+                          head_dim=128, o_dtype=B.UA_DTYPE_BF16, o_stride_tok=1024, o=4096)
+    a.partial_o[0] = 8192
+    a.partial_lse[0] = 8192
+    with pytest.raises(B.UaError):
+        B.ua_merge(a, None)
+    assert "partial set 1" in B.ua_last_error()
+    h = B.ua_create_problem(_desc())
+    try:
+        args = B.ua_run_args_t(q=16, k_cache=16, v_cache=16, o=None, block_table=16,
+                               seq_lens=16, cu_seqlens_q=16, num_seqs=2, max_seqlen_q=4,
+                               total_q=8, max_seqlen_k=512, block_table_stride=32,
+                               q_stride_tok=8 * 128, o_stride_tok=8 * 128, partial_o=256)
+        with pytest.raises(B.UaError):
+            B.ua_run(h, args, None)
+        assert "partial_lse" in B.ua_last_error()
+    finally:
+        B.ua_destroy_problem(h)

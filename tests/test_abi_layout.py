@@ -12,7 +12,7 @@ from varlen_attention_serving_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STRUCTS = {"ua_problem_desc_t": B.ua_problem_desc_t, "ua_run_args_t": B.ua_run_args_t,
-           "ua_plan_info_t": B.ua_plan_info_t}
+           "ua_plan_info_t": B.ua_plan_info_t, "ua_merge_args_t": B.ua_merge_args_t}
 
 
 def _c_layout(tmp_path):

@@ -27,8 +27,11 @@ UA_FLAG_WINDOW = 1 << 3
 UA_FLAG_SINKS = 1 << 4
 UA_FLAG_QQ_BIAS = 1 << 5
 UA_FLAG_DENSE_KV = 1 << 6
+UA_FLAG_BF16_PARTIALS = 1 << 7
 UA_FLAG_FORCE_2D = 1 << 8
 UA_FLAG_FORCE_3D = 1 << 9
+UA_PARTIAL_F32, UA_PARTIAL_BF16 = 0, 1
+UA_MAX_MERGE_SETS = 8
 
 STATUS_NAMES = {UA_OK: "UA_OK", UA_ERR_INVALID_ARG: "UA_ERR_INVALID_ARG",
                 UA_ERR_UNSUPPORTED: "UA_ERR_UNSUPPORTED", UA_ERR_WORKSPACE: "UA_ERR_WORKSPACE",
@@ -36,7 +39,7 @@ STATUS_NAMES = {UA_OK: "UA_OK", UA_ERR_INVALID_ARG: "UA_ERR_INVALID_ARG",
 
 # every symbol include/ua.h declares
 EXPORTS = ("ua_create_problem", "ua_workspace_size", "ua_query_plan", "ua_run",
-           "ua_run_no_alloc", "ua_destroy_problem", "ua_last_error", "ua_version")
+           "ua_run_no_alloc", "ua_merge", "ua_destroy_problem", "ua_last_error", "ua_version")
 
 
 class ua_problem_desc_t(ctypes.Structure):
@@ -88,6 +91,26 @@ class ua_run_args_t(ctypes.Structure):
         ("qq_bias", ctypes.c_void_p),
         ("qq_bias_stride", ctypes.c_int32),
         ("cu_seqlens_k", ctypes.c_void_p),
+        ("partial_o", ctypes.c_void_p),
+        ("partial_lse", ctypes.c_void_p),
+        ("partial_dtype", ctypes.c_int32),
+    ]
+
+
+class ua_merge_args_t(ctypes.Structure):
+    _fields_ = [
+        ("num_sets", ctypes.c_int32),
+        ("partial_dtype", ctypes.c_int32),
+        ("partial_o", ctypes.c_void_p * UA_MAX_MERGE_SETS),
+        ("partial_lse", ctypes.c_void_p * UA_MAX_MERGE_SETS),
+        ("total_q", ctypes.c_int64),
+        ("num_q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("o_dtype", ctypes.c_int32),
+        ("o_stride_tok", ctypes.c_int64),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -130,6 +153,8 @@ def _load():
     L.ua_run.restype = ctypes.c_int
     L.ua_run_no_alloc.argtypes = [vp, ctypes.POINTER(ua_run_args_t), vp]
     L.ua_run_no_alloc.restype = ctypes.c_int
+    L.ua_merge.argtypes = [ctypes.POINTER(ua_merge_args_t), vp]
+    L.ua_merge.restype = ctypes.c_int
     L.ua_destroy_problem.argtypes = [vp]
     L.ua_destroy_problem.restype = None
     L.ua_last_error.argtypes = []
@@ -179,6 +204,10 @@ def ua_run(problem, args: ua_run_args_t, stream) -> None:
 
 def ua_run_no_alloc(problem, args: ua_run_args_t, stream) -> None:
     _check(lib.ua_run_no_alloc(problem, ctypes.byref(args), stream))
+
+
+def ua_merge(args: ua_merge_args_t, stream) -> None:
+    _check(lib.ua_merge(ctypes.byref(args), stream))
 
 
 def ua_destroy_problem(problem) -> None:

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libua.so")
 
-SOURCES = ["ua_api.cpp", "ua_attn_d64.hip", "ua_attn_d128.hip", "ua_attn_d256.hip"]
+SOURCES = ["ua_api.cpp", "ua_attn_d64.hip", "ua_attn_d128.hip", "ua_attn_d256.hip",
+           "ua_merge.hip"]
 HEADERS = ["ua_internal.h", "ua_attn_impl.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

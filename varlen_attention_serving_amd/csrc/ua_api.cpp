@@ -56,6 +56,7 @@ struct ua_problem {
     int group;
     int log2_block;
     bool fp8;
+    bool ws_bf16;  // split partial o stored as bf16
     size_t ws_bytes;
     // a split batch runs its stream-K launch on a second stream, forked from
     // and joined back into the caller's (created on the first split run)
@@ -71,7 +72,9 @@ struct ua_problem {
 
 namespace {
 
-int row_bytes(const ua_problem& P) { return (P.d.head_dim + 2) * 4; }
+// workspace bytes of one partial row: o (f32, or bf16) then m and l (f32)
+int row_bytes(const ua_problem& P) { return P.d.head_dim * (P.ws_bf16 ? 2 : 4) + 8; }
+int o_elem_bytes(const ua_problem& P) { return P.ws_bf16 ? 2 : 4; }
 
 // One kernel launch of the plan (plus its reduce on the split path).
 struct Sub {
@@ -330,8 +333,8 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
         return fail(UA_ERR_UNSUPPORTED, "kv_dtype %d must equal q_dtype or be fp8 e4m3",
                     d.kv_dtype);
     const uint32_t known = UA_FLAG_CAUSAL | UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_WINDOW |
-                           UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_DENSE_KV | UA_FLAG_FORCE_2D |
-                           UA_FLAG_FORCE_3D;
+                           UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_DENSE_KV |
+                           UA_FLAG_BF16_PARTIALS | UA_FLAG_FORCE_2D | UA_FLAG_FORCE_3D;
     if (d.flags & ~known) return fail(UA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags & ~known);
     if ((d.flags & UA_FLAG_FORCE_2D) && (d.flags & UA_FLAG_FORCE_3D))
         return fail(UA_ERR_INVALID_ARG, "FORCE_2D and FORCE_3D are exclusive");
@@ -368,6 +371,7 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     // the kernels see a dense sequence as one block of 2^30 rows
     P->log2_block = dense ? 30 : ilog2(d.block_size);
     P->fp8 = d.kv_dtype == UA_DTYPE_FP8_E4M3;
+    P->ws_bf16 = (d.flags & UA_FLAG_BF16_PARTIALS) != 0;
     // split workspace: enough segments for the smallest tile (32 keys) and the
     // minimum segment length at the maxima, capped at 2 GiB (a larger batch
     // then gets fewer, longer segments)
@@ -486,9 +490,18 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
                    a->block_table_stride > std::max(d.max_blocks_per_seq, 1)))
         return fail(UA_ERR_INVALID_ARG, "block_table_stride %d outside [ceil(max_seqlen_k/b), %d]",
                     a->block_table_stride, d.max_blocks_per_seq);
-    if (!a->q || !a->k_cache || !a->v_cache || !a->o || !a->cu_seqlens_q ||
+    const bool partial = a->partial_o != nullptr;
+    if (!a->q || !a->k_cache || !a->v_cache || (!a->o && !partial) || !a->cu_seqlens_q ||
         (!dense && (!a->block_table || !a->seq_lens)))
         return fail(UA_ERR_INVALID_ARG, "null required device pointer");
+    if (partial) {
+        if (!a->partial_lse || ((uintptr_t)a->partial_lse & 3))
+            return fail(UA_ERR_INVALID_ARG, "partial_o needs a 4-byte aligned partial_lse");
+        if ((uintptr_t)a->partial_o & 15)
+            return fail(UA_ERR_INVALID_ARG, "partial_o must be 16-byte aligned");
+        if (a->partial_dtype != UA_PARTIAL_F32 && a->partial_dtype != UA_PARTIAL_BF16)
+            return fail(UA_ERR_INVALID_ARG, "partial_dtype %d unknown", a->partial_dtype);
+    }
     if (dense && (!a->cu_seqlens_k || ((uintptr_t)a->cu_seqlens_k & 3)))
         return fail(UA_ERR_INVALID_ARG, "dense K/V need a 4-byte aligned cu_seqlens_k");
     if ((d.flags & UA_FLAG_ALIBI) && !a->alibi_slopes)
@@ -545,6 +558,16 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
     base.out_scale = p->fp8 ? d.v_scale : 1.0f;
     base.small_block_q = pl.small_block_q;
     base.sk_heads = 1;
+    base.ws_bf16 = p->ws_bf16;
+    if (partial) {
+        // merge-ready states without the sinks, which ua_merge joins once
+        base.part_o = a->partial_o;
+        base.part_lse = a->partial_lse;
+        base.part_bf16 = a->partial_dtype == UA_PARTIAL_BF16;
+        base.flags &= ~(uint32_t)UA_FLAG_SINKS;
+        base.sinks = nullptr;
+        base.lse = nullptr;
+    }
 
     // workspace: [segmented partials][stream-K partials], both 256-byte aligned
     if (no_alloc && (a->workspace || a->workspace_bytes))
@@ -656,10 +679,10 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
         l.reduce_rows = a->total_q * d.num_q_heads;
         l.sk_waves_cap = (int)sk_extra;
         if (g.path == 3 && g.stream_k) {
-            float* ws = reinterpret_cast<float*>(static_cast<char*>(ws_base) + seg_bytes);
+            char* ws = static_cast<char*>(ws_base) + seg_bytes;
             const size_t rows = ((size_t)a->num_seqs * d.num_kv_heads + sk_extra) * kp.rows_used;
             kp.ws_o = ws;
-            kp.ws_m = ws + rows * d.head_dim;
+            kp.ws_m = reinterpret_cast<float*>(ws + rows * d.head_dim * o_elem_bytes(*p));
             kp.ws_l = kp.ws_m + rows;
             // enumerate reduce rows by (sequence, head, position) when most
             // tokens belong to the other launch
@@ -667,11 +690,11 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
             kp.reduce_by_seq = g.class_mode == 1 && by_seq < l.reduce_rows;
             if (kp.reduce_by_seq) l.reduce_rows = by_seq;
         } else if (g.path == 3) {
-            const size_t rows = (size_t)a->total_q * d.num_q_heads;
-            float* ws = static_cast<float*>(ws_base);
+            const size_t rows = (size_t)a->total_q * d.num_q_heads * g.num_segments;
+            char* ws = static_cast<char*>(ws_base);
             kp.ws_o = ws;
-            kp.ws_m = ws + rows * g.num_segments * d.head_dim;
-            kp.ws_l = kp.ws_m + rows * g.num_segments;
+            kp.ws_m = reinterpret_cast<float*>(ws + rows * d.head_dim * o_elem_bytes(*p));
+            kp.ws_l = kp.ws_m + rows;
         }
         // timing events of a single launch: [0] before the kernel, [1] after
         // it, [2] after its reduce; a split batch records its own around both
@@ -716,6 +739,49 @@ ua_status_t ua_run(ua_problem_t p, const ua_run_args_t* a, void* stream) {
 ua_status_t ua_run_no_alloc(ua_problem_t p, const ua_run_args_t* a, void* stream) {
     g_error.clear();
     return run_impl(p, a, stream, true);
+}
+
+ua_status_t ua_merge(const ua_merge_args_t* a, void* stream) {
+    g_error.clear();
+    if (!a) return fail(UA_ERR_INVALID_ARG, "null merge arguments");
+    if (a->num_sets < 1 || a->num_sets > UA_MAX_MERGE_SETS)
+        return fail(UA_ERR_INVALID_ARG, "num_sets %d outside [1, %d]", a->num_sets,
+                    UA_MAX_MERGE_SETS);
+    if (a->partial_dtype != UA_PARTIAL_F32 && a->partial_dtype != UA_PARTIAL_BF16)
+        return fail(UA_ERR_INVALID_ARG, "partial_dtype %d unknown", a->partial_dtype);
+    if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+        return fail(UA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", a->head_dim);
+    if (a->num_q_heads <= 0 || a->total_q < 0)
+        return fail(UA_ERR_INVALID_ARG, "merge shape out of range");
+    if (a->o_dtype != UA_DTYPE_BF16 && a->o_dtype != UA_DTYPE_F16)
+        return fail(UA_ERR_INVALID_ARG, "o_dtype %d must be bf16 or f16", a->o_dtype);
+    if (a->o_stride_tok < (int64_t)a->num_q_heads * a->head_dim || a->o_stride_tok % 8)
+        return fail(UA_ERR_INVALID_ARG, "o_stride_tok must be >= H_q * head_dim and a multiple of 8");
+    if (a->total_q == 0) return UA_OK;
+    if (!a->o || ((uintptr_t)a->o & 15)) return fail(UA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+    if ((uintptr_t)a->lse & 3 || (uintptr_t)a->sinks & 3)
+        return fail(UA_ERR_INVALID_ARG, "lse and sinks must be 4-byte aligned");
+    UaMergeParams mp{};
+    for (int i = 0; i < a->num_sets; ++i) {
+        if (!a->partial_o[i] || !a->partial_lse[i] || ((uintptr_t)a->partial_o[i] & 15) ||
+            ((uintptr_t)a->partial_lse[i] & 3))
+            return fail(UA_ERR_INVALID_ARG, "partial set %d: null or misaligned pointer", i);
+        mp.o[i] = a->partial_o[i];
+        mp.lse[i] = a->partial_lse[i];
+    }
+    mp.num_sets = a->num_sets;
+    mp.part_bf16 = a->partial_dtype == UA_PARTIAL_BF16;
+    mp.rows = a->total_q * a->num_q_heads;
+    mp.num_q_heads = a->num_q_heads;
+    mp.head_dim = a->head_dim;
+    mp.out_dtype = a->o_dtype;
+    mp.out = a->o;
+    mp.out_stride_tok = a->o_stride_tok;
+    mp.out_lse = a->lse;
+    mp.sinks = a->sinks;
+    const hipError_t e = ua_launch_merge(mp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(UA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+    return UA_OK;
 }
 
 }  // extern "C"

@@ -804,19 +804,30 @@ __device__ __forceinline__ Frag padded_frag(int lane) {
     return f;
 }
 
-// Un-normalised partial of the lane's row: o (fp32), the running max m (log2
-// units) and the denominator l, at workspace row `rid`.
+// Four consecutive fp32 values of a partial row, stored as fp32 or (bf16)
+// rounded to nearest even; `base` is the row's first element.
+__device__ __forceinline__ void store4(void* base, int64_t elem, f32x4 v, bool bf16) {
+    if (bf16) {
+        const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(base) + elem) = b;
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(base) + elem) = v;
+    }
+}
+
+// Un-normalised partial of the lane's row: o (fp32, or bf16 with ws_bf16),
+// the running max m (log2 units) and the denominator l, at workspace row `rid`.
 template <int D>
 __device__ __forceinline__ void write_partial(const UaKernelParams& p, int64_t rid, int half,
                                               const f32x16 (&oacc)[D / 32], float m, float l) {
-    float* wo = p.ws_o + rid * D + 4 * half;
+    const int64_t e0 = rid * D + 4 * half;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
             f32x4 v = {oacc[dt][4 * ig], oacc[dt][4 * ig + 1], oacc[dt][4 * ig + 2],
                        oacc[dt][4 * ig + 3]};
-            *reinterpret_cast<f32x4*>(wo + 32 * dt + 8 * ig) = v;
+            store4(p.ws_o, e0 + 32 * dt + 8 * ig, v, p.ws_bf16);
         }
     if (half == 0) {
         p.ws_m[rid] = m;
@@ -898,6 +909,19 @@ __device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowIn
     if (SPLIT) {
         const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
         write_partial<D>(p, rid, half, oacc, m_run, l_tot);
+    } else if (p.part_o) {
+        // the row's merge-ready state over this call's keys: o / l and its LSE
+        const int64_t row = (int64_t)ri.tok * p.num_q_heads + ri.head;
+        if (half == 0) p.part_lse[row] = row_lse(m_run, l_tot);
+        const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                f32x4 v = {oacc[dt][4 * ig] * inv, oacc[dt][4 * ig + 1] * inv,
+                           oacc[dt][4 * ig + 2] * inv, oacc[dt][4 * ig + 3] * inv};
+                store4(p.part_o, row * D + 4 * half + 32 * dt + 8 * ig, v, p.part_bf16);
+            }
     } else {
         if (p.lse && half == 0) p.lse[(int64_t)ri.tok * p.num_q_heads + ri.head] = row_lse(m_run, l_tot);
         const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
@@ -1743,10 +1767,9 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
                 const int64_t unit = (int64_t)pc.s * sk_groups(p) + pc.h;
                 const int64_t slot = (unit + j) * p.sk_heads + wave;
                 const int64_t rid = slot * p.rows_used + (lane & 15);
-                float* wo = p.ws_o + rid * D + 4 * grp;
 #pragma unroll
                 for (int db = 0; db < G::NDB; ++db)
-                    *reinterpret_cast<f32x4*>(wo + 16 * db) = oacc[db];
+                    store4(p.ws_o, rid * D + 4 * grp + 16 * db, oacc[db], p.ws_bf16);
                 if (grp == 0) {
                     p.ws_m[rid] = m_run;
                     p.ws_l[rid] = l_tot;
@@ -1770,6 +1793,25 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
 // One wave per (token, query head); four per workgroup.  Partials are merged
 // in a fixed order, four at a time with all their loads issued together, so
 // the result is the same on every run.
+// N consecutive partial values (f32, or bf16 when `bf16`) from element
+// `elem` of `base` as one vector load of 4 N or 2 N bytes (elem is a
+// multiple of N and the buffer 16-byte aligned).
+template <int N>
+__device__ __forceinline__ void load_row_part(const void* base, int64_t elem, bool bf16,
+                                              float (&out)[N]) {
+    if (bf16) {
+        typedef __bf16 vb __attribute__((ext_vector_type(N)));
+        const vb x = *reinterpret_cast<const vb*>(static_cast<const __bf16*>(base) + elem);
+#pragma unroll
+        for (int e = 0; e < N; ++e) out[e] = (float)x[e];
+    } else {
+        typedef float vf __attribute__((ext_vector_type(N)));
+        const vf x = *reinterpret_cast<const vf*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+        for (int e = 0; e < N; ++e) out[e] = x[e];
+    }
+}
+
 template <int D, typename QT>
 __device__ __forceinline__ void merge_partials(const UaKernelParams& p, int64_t first, int64_t stride,
                                                int count, int64_t j0, int64_t T, int64_t W, bool sk,
@@ -1793,9 +1835,9 @@ __device__ __forceinline__ void merge_partials(const UaKernelParams& p, int64_t 
             const int64_t rid = first + (int64_t)(live ? g : 0) * stride;
             mg[u] = live ? p.ws_m[rid] : -INFINITY;
             lg[u] = live ? p.ws_l[rid] : 0.0f;
-            const float* src = p.ws_o + rid * D + lane * EPL;
+            load_row_part<EPL>(p.ws_o, rid * D + lane * EPL, p.ws_bf16, og[u]);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) og[u][e] = live ? src[e] : 0.0f;
+            for (int e = 0; e < EPL; ++e) og[u][e] = live ? og[u][e] : 0.0f;
         }
         float bm = mx;
 #pragma unroll
@@ -1815,6 +1857,21 @@ __device__ __forceinline__ void merge_partials(const UaKernelParams& p, int64_t 
         mx = bm;
     }
     const float inv = L > 0.0f ? p.out_scale / L : 0.0f;
+    if (p.part_o) {
+        // partial-output mode: the merged row's o / L and its LSE
+        const int64_t row = (int64_t)tok * p.num_q_heads + head;
+        if (lane == 0) p.part_lse[row] = row_lse(mx, L);
+        if (p.part_bf16) {
+            __bf16* dst = static_cast<__bf16*>(p.part_o) + row * D + lane * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dst[e] = (__bf16)(acc[e] * inv);
+        } else {
+            float* dst = static_cast<float*>(p.part_o) + row * D + lane * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
+        }
+        return;
+    }
     if (p.lse && lane == 0) p.lse[(int64_t)tok * p.num_q_heads + head] = row_lse(mx, L);
     QT* dst = reinterpret_cast<QT*>(p.o) + (int64_t)tok * p.o_stride_tok + (int64_t)head * D +
               lane * EPL;

@@ -19,7 +19,8 @@ struct UaKernelParams {
     const float* qq_bias;     // [q_local][k_local] query-section bias (QQ_BIAS flag)
     const int32_t* cu_k;      // dense K/V: first row of each sequence (else NULL)
     int qq_stride;
-    float* ws_o;              // split partials: un-normalised o  [rows, NS, D]
+    void* ws_o;               // split partials: un-normalised o  [rows, NS, D] (f32, or
+                              // bf16 when ws_bf16)
     float* ws_m;              //                 running max (log2 units) [rows, NS]
     float* ws_l;              //                 denominator           [rows, NS]
     int64_t q_stride_tok;     // elements
@@ -49,6 +50,13 @@ struct UaKernelParams {
     int32_t small_block_q;    // query positions of a single-wave q-block (32 / g)
     int32_t reduce_by_seq;    // stream-K reduce rows enumerated as (seq, head, i)
     int32_t sk_heads;         // stream-K: kv heads one worker serves together (a wave each)
+    int32_t ws_bf16;          // split partials' o stored as bf16 (UA_FLAG_BF16_PARTIALS)
+    // partial-output mode (NULL: normal run): each row's normalised o over
+    // this call's keys, [total_q, H_q, D] f32 or bf16, and its natural-log
+    // LSE [total_q, H_q], both without sinks, instead of O
+    void* part_o;
+    float* part_lse;
+    int32_t part_bf16;
 };
 
 // Upper bound on stream-K workers (sizes the workspace before the device is known).
@@ -74,6 +82,24 @@ struct UaLaunch {
                           // workspace holds that many slots beyond one per (seq, kv head))
 };
 
+// Caller-held partial states merged by ua_merge (one wave per row).
+constexpr int kMaxMergeSets = 8;
+struct UaMergeParams {
+    const void* o[kMaxMergeSets];    // per set: [rows, D] o / l (f32 or bf16)
+    const float* lse[kMaxMergeSets]; // per set: [rows] natural-log LSE
+    int num_sets;
+    int part_bf16;
+    int64_t rows;                    // total_q * H_q
+    int num_q_heads;
+    int head_dim;
+    int out_dtype;                   // UA_DTYPE_BF16 / UA_DTYPE_F16
+    void* out;                       // [total_q, H_q, D], token stride out_stride_tok
+    int64_t out_stride_tok;
+    float* out_lse;                  // optional [rows]
+    const float* sinks;              // optional [H_q] natural-log logits
+};
+
+hipError_t ua_launch_merge(const UaMergeParams& p, hipStream_t s);
 hipError_t ua_launch_d64(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
 hipError_t ua_launch_d128(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
 hipError_t ua_launch_d256(const UaKernelParams& p, const UaLaunch& l, hipStream_t s);
