@@ -865,6 +865,7 @@ __device__ __forceinline__ const int32_t* table_row(const UaKernelParams& p, int
 struct QBlockWork {
     int s, q_start, q_len, p0, s_k, t_lo, t_hi;
     KeyRange kr;
+    bool whole;  // the workgroup covers the q-block's whole key range (writes O)
 };
 
 template <int BN, bool SPLIT>
@@ -886,12 +887,15 @@ __device__ __forceinline__ bool qblock_work(const UaKernelParams& p, int slot, i
     w.kr = key_range(p.flags, p.window, w.s_k, w.s_k - w.q_len, w.p0, p_last);
     w.t_lo = w.kr.lo / BN;
     w.t_hi = (w.kr.hi + BN - 1) / BN;
+    w.whole = true;
     if (SPLIT) {
         // this segment's run of the q-block's tiles; the reduce derives the
-        // same piece count
+        // same piece count (and leaves a one-piece q-block's rows, written
+        // here as O, alone)
         const int n = w.t_hi - w.t_lo;
         const int pieces = seg_pieces(n, p.num_segments, p.tiles_per_seg);
         if (seg >= pieces) return false;
+        w.whole = pieces == 1;
         w.t_hi = w.t_lo + (int)((int64_t)(seg + 1) * n / pieces);
         w.t_lo = w.t_lo + (int)((int64_t)seg * n / pieces);
     }
@@ -899,21 +903,35 @@ __device__ __forceinline__ bool qblock_work(const UaKernelParams& p, int slot, i
 }
 
 // A wave's rows after the last tile: normalised O, or the split partial.
+// A split workgroup that covers its q-block's whole key range (`whole`)
+// finishes like the 2D path; its sink, which a split run leaves to the
+// reduce, joins here as one more softmax term: (m, l) <- (max(m, sink),
+// l 2^(m - m') + 2^(sink - m')), O scaled by 2^(m - m').
 template <int D, typename QT, bool SPLIT>
 __device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowInfo& ri, int half,
-                                            int seg, const f32x16 (&oacc)[D / 32], float m_run,
-                                            float l_run) {
+                                            int seg, bool whole, const f32x16 (&oacc)[D / 32],
+                                            float m_run, float l_run) {
     typedef QType<QT> Q;
-    const float l_tot = l_run + xor32(l_run);
+    float l_tot = l_run + xor32(l_run);
     if (!ri.ok) return;
-    if (SPLIT) {
+    if (SPLIT && !whole) {
         const int64_t rid = ((int64_t)ri.tok * p.num_q_heads + ri.head) * p.num_segments + seg;
         write_partial<D>(p, rid, half, oacc, m_run, l_tot);
-    } else if (p.part_o) {
+        return;
+    }
+    float alpha = 1.0f;
+    if (SPLIT && (p.flags & UA_FLAG_SINKS)) {
+        const float s2 = p.sinks[ri.head] * kLog2e;
+        const float m2 = fmaxf(m_run, s2);
+        alpha = fast_exp2(m_run - m2);
+        l_tot = l_tot * alpha + fast_exp2(s2 - m2);
+        m_run = m2;
+    }
+    if (p.part_o) {
         // the row's merge-ready state over this call's keys: o / l and its LSE
         const int64_t row = (int64_t)ri.tok * p.num_q_heads + ri.head;
         if (half == 0) p.part_lse[row] = row_lse(m_run, l_tot);
-        const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+        const float inv = l_tot > 0.0f ? p.out_scale * alpha / l_tot : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -924,7 +942,7 @@ __device__ __forceinline__ void finish_rows(const UaKernelParams& p, const RowIn
             }
     } else {
         if (p.lse && half == 0) p.lse[(int64_t)ri.tok * p.num_q_heads + ri.head] = row_lse(m_run, l_tot);
-        const float inv = l_tot > 0.0f ? p.out_scale / l_tot : 0.0f;
+        const float inv = l_tot > 0.0f ? p.out_scale * alpha / l_tot : 0.0f;
         QT* op = reinterpret_cast<QT*>(p.o) + (int64_t)ri.tok * p.o_stride_tok +
                  (int64_t)ri.head * D + 4 * half;
 #pragma unroll
@@ -1027,7 +1045,7 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
     }
 
     if (!wave_active) return;
-    finish_rows<D, QT, SPLIT>(p, ri, half, seg, oacc, m_run, l_run);
+    finish_rows<D, QT, SPLIT>(p, ri, half, seg, qb.whole, oacc, m_run, l_run);
 }
 
 // The same q-block work for 16-bit K/V with four waves and block sizes of at
@@ -1144,7 +1162,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
     }
 
     if (!wave_active) return;
-    finish_rows<D, QT, SPLIT>(p, ri, half, seg, oacc, m_run, l_run);
+    finish_rows<D, QT, SPLIT>(p, ri, half, seg, qb.whole, oacc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -1965,6 +1983,7 @@ __global__ __launch_bounds__(256) void ua_reduce_kernel(UaKernelParams p, int64_
         const int t_lo = kr.lo / p.tile_n;
         const int t_hi = (kr.hi + p.tile_n - 1) / p.tile_n;
         const int count = seg_pieces(t_hi - t_lo, p.num_segments, p.tiles_per_seg);
+        if (count == 1) return;  // one piece: the attention kernel wrote the row
         merge_partials<D, QT>(p, row * p.num_segments, 1, count, 0, 1, 1, false, tok, head);
     }
 }
@@ -2108,7 +2127,9 @@ template <int D, typename QT, bool FP8, int XF>
 hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
     if (l.waves == 1 && l.tile_n == 32) return launch_if_built<D, 1, 32, QT, FP8, XF>(p, l, st);
     if (l.waves == 4 && l.tile_n == 32) return launch_if_built<D, 4, 32, QT, FP8, XF>(p, l, st);
-    if constexpr (D <= 128) {
+    if constexpr (D == 64) {
+        // 64-key tiles: four-wave fp8 tiles at d = 64 (a tile holds whole
+        // passes of 256 threads' 16-byte chunks)
         if (l.waves == 4 && l.tile_n == 64) return launch_if_built<D, 4, 64, QT, FP8, XF>(p, l, st);
     }
     return hipErrorInvalidValue;
