@@ -460,6 +460,44 @@ def clocks_under(runner, seconds, ms_per_step, flush=None):
     return info
 
 
+def single_thread_oracle(names=("tiny_varlen", "decode_batch"), budget_s=3.0):
+    """The oracle on one host thread: the whole tiny batch, and whole
+    sequences of the decode batch for about `budget_s`, in the metric's units."""
+    import oracle
+    out = {}
+    for name in names:
+        from varlen_attention_serving_amd import workloads as W
+        w = W.named(name)
+        if name == "tiny_varlen":
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < 0.5:
+                oracle.attention(w, nthreads=1)
+                reps += 1
+            sec = (time.perf_counter() - t0) / reps
+            a = algorithmic_work(w)
+            out[name] = {"seconds_per_batch": round(sec, 6), "GB/s": round(a["bytes"] / sec / 1e9, 6),
+                         "threads": 1, "sample": f"the whole batch, {reps} runs"}
+        else:
+            order = np.random.default_rng(7).permutation(w.num_seqs)
+            done = 0
+            t = 0.0
+            seqs = 0
+            for s in order:
+                lo, hi = int(w.cu_seqlens_q[s]), int(w.cu_seqlens_q[s + 1])
+                rows = np.arange(lo * w.num_q_heads, hi * w.num_q_heads, dtype=np.int64)
+                t0 = time.perf_counter()
+                oracle.rows(w, rows, nthreads=1)
+                t += time.perf_counter() - t0
+                done += algorithmic_work(_subset(w, s))["bytes"]
+                seqs += 1
+                if t >= budget_s:
+                    break
+            out[name] = {"GB/s": round(done / t / 1e9, 6), "threads": 1, "seconds": round(t, 2),
+                         "sample": f"{seqs} whole sequences of the batch (all rows and heads)"}
+    return out
+
+
 def cpu_object(w, bound, unit, budget_s, by_rows):
     print(f"[bench] oracle CPU baseline on {w.name} (~{budget_s:.0f} s)", file=sys.stderr,
           flush=True)
@@ -514,6 +552,8 @@ def main():
                     help="split-KV segment length in KV tiles (0 = the plan's choice)")
     ap.add_argument("--bf16-partials", action="store_true",
                     help="keep the split-KV partial o in bf16 (UA_FLAG_BF16_PARTIALS)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="run a 2D LDS-ring launch on the persistent schedule (UA_FLAG_PERSISTENT)")
     ap.add_argument("--clock-seconds", type=float, default=1.0,
                     help="seconds of untimed replay after timing during which amdsmi "
                          "samples the GPU clocks (0 = skip)")
@@ -570,7 +610,8 @@ def main():
 
     from varlen_attention_serving_amd import binding as B
     r = Runner(args.workload, args.force, args.segment_tiles,
-               B.UA_FLAG_BF16_PARTIALS if args.bf16_partials else 0)
+               (B.UA_FLAG_BF16_PARTIALS if args.bf16_partials else 0) |
+               (B.UA_FLAG_PERSISTENT if args.persistent else 0))
     flush = make_read_flush(torch) if (args.cold or "cold" in extras) else None
     t = r.time(args.steps, args.warmup, args.event_every, flush if args.cold else None)
     f = r.figures(t)
@@ -588,6 +629,7 @@ def main():
         "attention_kernel_ms_min": round(float(np.min(t["attn"])), 5),
         "cache": "cold (read-only 1 GiB flush before each step)" if args.cold else "warm",
         "split_partials": "bf16" if args.bf16_partials else "f32",
+        "schedule": "persistent" if args.persistent else "grid",
         "roofline_frac_whole_step": round(max(r.t_hbm, r.t_mfma) / (ms_per_step * 1e-3), 4),
         "roofline_frac_whole_forward_events": round(f["frac_whole_forward"], 4),
         "clocks": clock_info,
@@ -628,6 +670,8 @@ def main():
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_object(r.w, r.bound, f["unit"], args.cpu_seconds,
                                          by_rows=False)
+        if args.workload == "decode_batch":
+            out["cpu_baseline"]["single_thread"] = single_thread_oracle()
     r.close()
     del flush
 

@@ -62,7 +62,16 @@ enum {
                                     and a smaller ua_workspace_size; each partial is
                                     rounded to bf16 (2^-9 relative) before the merge */
     UA_FLAG_FORCE_2D = 1u << 8, /* testing/benchmarking: bypass the shape rule */
-    UA_FLAG_FORCE_3D = 1u << 9
+    UA_FLAG_FORCE_3D = 1u << 9,
+    UA_FLAG_PERSISTENT = 1u << 10 /* a lone 2D launch of four-wave q-blocks on the LDS
+                                    ring runs on the persistent schedule of section
+                                    8.2 of the unified page: one workgroup per resident
+                                    slot drawing q-blocks, heaviest first, from eight
+                                    work queues (one per XCD, so a kv head's K/V stays
+                                    in one L2); results are bitwise those of the
+                                    default grid.  Needs 256 bytes of workspace
+                                    (included in ua_workspace_size); other launches
+                                    keep the default grid. */
 };
 
 /* Element type of caller-held partial states (ua_run_args_t.partial_o and

@@ -30,6 +30,7 @@ UA_FLAG_DENSE_KV = 1 << 6
 UA_FLAG_BF16_PARTIALS = 1 << 7
 UA_FLAG_FORCE_2D = 1 << 8
 UA_FLAG_FORCE_3D = 1 << 9
+UA_FLAG_PERSISTENT = 1 << 10
 UA_PARTIAL_F32, UA_PARTIAL_BF16 = 0, 1
 UA_MAX_MERGE_SETS = 8
 

@@ -31,6 +31,7 @@ constexpr int kSplitWorkgroupsPerCU = 8;
 constexpr int kWideResidentPerCU = 3;   // four-wave workgroups resident per CU
 constexpr int kMaxWideSegments = 2;
 constexpr size_t kWorkspaceCap = size_t(2) << 30;
+constexpr size_t kQueueBytes = 256;     // persistent schedule: queue counters
 constexpr float kLog2e = 1.4426950408889634f;
 
 thread_local std::string g_error;
@@ -334,7 +335,8 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
                     d.kv_dtype);
     const uint32_t known = UA_FLAG_CAUSAL | UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_WINDOW |
                            UA_FLAG_SINKS | UA_FLAG_QQ_BIAS | UA_FLAG_DENSE_KV |
-                           UA_FLAG_BF16_PARTIALS | UA_FLAG_FORCE_2D | UA_FLAG_FORCE_3D;
+                           UA_FLAG_BF16_PARTIALS | UA_FLAG_PERSISTENT | UA_FLAG_FORCE_2D |
+                           UA_FLAG_FORCE_3D;
     if (d.flags & ~known) return fail(UA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags & ~known);
     if ((d.flags & UA_FLAG_FORCE_2D) && (d.flags & UA_FLAG_FORCE_3D))
         return fail(UA_ERR_INVALID_ARG, "FORCE_2D and FORCE_3D are exclusive");
@@ -387,6 +389,9 @@ ua_status_t ua_create_problem(const ua_problem_desc_t* desc, ua_problem_t* out) 
     // geometry, at most 32 rows per q-block)
     P->ws_bytes = ((per_seg * (size_t)std::min(ns_max, ns_cap) + 255) & ~size_t(255)) +
                   stream_k_bytes(*P, std::max(d.max_num_seqs, 1), 32);
+    // the persistent schedule's queue counters (a 2D launch, which uses no
+    // other workspace)
+    if (d.flags & UA_FLAG_PERSISTENT) P->ws_bytes = std::max<size_t>(P->ws_bytes, kQueueBytes);
     *out = P;
     return UA_OK;
 }
@@ -604,6 +609,12 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
     }
     if (sk_rows) sk_bytes = stream_k_bytes(*p, a->num_seqs, sk_rows, sk_extra);
     need = seg_bytes + sk_bytes;
+    // the persistent schedule applies to a lone 2D launch of four-wave
+    // q-blocks (the LDS-ring kernel takes it; others keep the default grid)
+    const Sub& g0 = pl.sub[pl.n - 1];
+    const bool persistent = (d.flags & UA_FLAG_PERSISTENT) && pl.n == 1 && g0.path == 2 &&
+                            g0.waves == 4 && (int64_t)g0.grid[0] * g0.grid[1] < (int64_t(1) << 30);
+    if (persistent) need = std::max(need, kQueueBytes);
     void* ws_base = a->workspace;
     if (no_alloc) {
         if (need > kScratchBytes)
@@ -678,6 +689,10 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
         for (int j = 0; j < 3; ++j) l.grid[j] = g.grid[j];
         l.reduce_rows = a->total_q * d.num_q_heads;
         l.sk_waves_cap = (int)sk_extra;
+        if (persistent) {
+            l.persistent = 1;
+            kp.queue = static_cast<int32_t*>(ws_base);
+        }
         if (g.path == 3 && g.stream_k) {
             char* ws = static_cast<char*>(ws_base) + seg_bytes;
             const size_t rows = ((size_t)a->num_seqs * d.num_kv_heads + sk_extra) * kp.rows_used;

@@ -1052,26 +1052,18 @@ __global__ __launch_bounds__(NW * 64, min_waves_per_simd(D, NW)) void ua_attn_ke
 // least ROWS_PER_OP keys: tiles arrive through the LDS ring instead of
 // registers (STAGES - 1 tiles in flight, one barrier per tile).
 template <int D, typename QT, bool SPLIT, int XF>
-__global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_kernel(UaKernelParams p) {
+__device__ __forceinline__ void lds_qblock(const UaKernelParams& p, unsigned short* tiles, int hk,
+                                           int slot, int seg) {
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
     typedef LdsGeom<D> L;
     constexpr int BN = L::BN;
     constexpr int S = L::STAGES;
 
-    __shared__ __attribute__((aligned(1024))) unsigned short tiles[S * 2 * L::TILE_ELEMS];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
-
-    int hk, slot, seg;
-    if (SPLIT) {
-        slot = blockIdx.x; hk = blockIdx.y; seg = blockIdx.z;
-    } else {
-        hk = blockIdx.x; slot = blockIdx.y; seg = 0;
-    }
 
     QBlockWork qb;
     if (!qblock_work<BN, SPLIT>(p, slot, seg, qb)) return;
@@ -1163,6 +1155,53 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
 
     if (!wave_active) return;
     finish_rows<D, QT, SPLIT>(p, ri, half, seg, qb.whole, oacc, m_run, l_run);
+}
+
+template <int D, typename QT, bool SPLIT, int XF>
+__global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_kernel(UaKernelParams p) {
+    typedef LdsGeom<D> L;
+    __shared__ __attribute__((aligned(1024))) unsigned short tiles[L::STAGES * 2 * L::TILE_ELEMS];
+    if (SPLIT)
+        lds_qblock<D, QT, SPLIT, XF>(p, tiles, blockIdx.y, blockIdx.x, blockIdx.z);
+    else
+        lds_qblock<D, QT, SPLIT, XF>(p, tiles, blockIdx.x, blockIdx.y, 0);
+}
+
+// Persistent schedule of the same 2D work (UA_FLAG_PERSISTENT): one
+// workgroup per resident slot, each taking q-blocks until none are left.
+// The work items keep the default grid's order, item = slot * H_k + h_k (a
+// sequence's heaviest q-block first), and are dealt from kPersistQueues
+// queues by item mod kPersistQueues.  Workgroup j draws from queue
+// j mod kPersistQueues: the dispatcher deals a launch's workgroups to the
+// XCDs round robin, so with H_k = 8 each XCD serves one kv head, whose K/V
+// then stays in that XCD's L2, as in the default grid, while the queue
+// balances the ragged q-blocks dynamically (the item order is fixed, so
+// every q-block is computed exactly as in the default grid).
+template <int D, typename QT, int XF>
+__global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_persist_kernel(UaKernelParams p) {
+    typedef LdsGeom<D> L;
+    __shared__ __attribute__((aligned(1024))) unsigned short tiles[L::STAGES * 2 * L::TILE_ELEMS];
+    __shared__ int next_item;
+    const int q = blockIdx.x % kPersistQueues;
+    const int64_t n_items = (int64_t)p.num_kv_heads * p.persist_slots;
+    for (;;) {
+        if (threadIdx.x == 0) next_item = q + kPersistQueues * atomicAdd(&p.queue[q], 1);
+        __syncthreads();
+        const int64_t item = __builtin_amdgcn_readfirstlane(next_item);  // uniform: scalar copies
+        // every wave has the item (and is done with the previous one's LDS)
+        // before the next draw overwrites it
+        __syncthreads();
+        if (item >= n_items) break;
+        lds_qblock<D, QT, false, XF>(p, tiles, (int)(item % p.num_kv_heads),
+                                     (int)(item / p.num_kv_heads), 0);
+    }
+}
+
+// Clears the persistent schedule's queue counters (a kernel rather than a
+// memset, so a caller may capture the run in a graph).
+template <int N>
+__global__ __launch_bounds__(64) void ua_queue_reset_kernel(int32_t* queue) {
+    if (threadIdx.x < N) queue[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -2090,8 +2129,20 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         if constexpr (ring_built) {
             if (ring && split)
                 hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, true, XF>), grid, dim3(256), 0, st, p);
-            if (ring && !split)
+            if (ring && !split && l.persistent) {
+                // as many workgroups as are resident at once, at most one per item
+                auto kern = ua_attn_persist_kernel<D, QT, XF>;
+                const int64_t items = (int64_t)grid.x * grid.y;
+                p.persist_slots = (int32_t)grid.y;
+                // every queue that holds items gets at least one workgroup
+                int64_t wgs = std::min<int64_t>(items, resident_workgroups(kern, 4));
+                if (items >= kPersistQueues)
+                    wgs = std::max<int64_t>(kPersistQueues, wgs / kPersistQueues * kPersistQueues);
+                hipLaunchKernelGGL(ua_queue_reset_kernel<kPersistQueues>, dim3(1), dim3(64), 0, st, p.queue);
+                hipLaunchKernelGGL(kern, dim3((unsigned)std::max<int64_t>(wgs, 1)), dim3(256), 0, st, p);
+            } else if (ring && !split) {
                 hipLaunchKernelGGL((ua_attn_lds_kernel<D, QT, false, XF>), grid, dim3(256), 0, st, p);
+            }
         }
         if (!ring && split)
             hipLaunchKernelGGL((ua_attn_kernel<D, NW, BN, QT, FP8, true, XF>), grid, dim3(NW * 64),

@@ -57,7 +57,12 @@ struct UaKernelParams {
     void* part_o;
     float* part_lse;
     int32_t part_bf16;
+    int32_t* queue;           // persistent schedule: kPersistQueues work-queue counters
+    int32_t persist_slots;    // persistent schedule: q-block slots per kv head
 };
+
+// Work queues of the persistent 2D schedule (one per XCD of an MI355X).
+constexpr int kPersistQueues = 8;
 
 // Upper bound on stream-K workers (sizes the workspace before the device is known).
 constexpr int kMaxStreamKWorkers = 8192;
@@ -80,6 +85,7 @@ struct UaLaunch {
     hipEvent_t events[3]; // optional: before attention, between kernels, at the end
     int sk_waves_cap;     // stream-K: at most this many workers * waves per worker (the
                           // workspace holds that many slots beyond one per (seq, kv head))
+    int persistent;       // 2D LDS-ring launch on the persistent schedule
 };
 
 // Caller-held partial states merged by ua_merge (one wave per row).
