@@ -323,15 +323,17 @@ def _visible(w, s):
 class Runner:
     """One workload on the device: its batch, problem handle and plan."""
 
-    def __init__(self, name, force="auto", segment_tiles=0, extra_flags=0):
+    def __init__(self, name, force="auto", segment_tiles=0, extra_flags=0, w=None):
         from varlen_attention_serving_amd import binding as B
         from varlen_attention_serving_amd import device as D
         from varlen_attention_serving_amd import workloads as W
         import torch
         self.B, self.torch = B, torch
-        print(f"[bench] generating {name}", file=sys.stderr, flush=True)
         self.name = name
-        self.w = w = W.named(name)
+        if w is None:
+            print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+            w = W.named(name)
+        self.w = w
         extra = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D}[force] | extra_flags
         self.batch = D.DeviceBatch(w)
         self.ua = D.UnifiedAttention(D.problem_desc(w, extra, split_segment_tiles=segment_tiles))
@@ -516,6 +518,56 @@ def cpu_object(w, bound, unit, budget_s, by_rows):
             "sample": sample}
 
 
+def part_batches(w):
+    """The parts of a batch that `--parts` times: the decode-shaped sequences
+    alone (q_len * g <= 32: rows of one single-wave q-block), the others
+    alone, and the whole batch with each optional feature switched off."""
+    import dataclasses
+    parts = [("all", w)]
+    dec = [s for s in range(w.num_seqs) if int(w.q_lens[s]) * w.group <= 32]
+    wide = [s for s in range(w.num_seqs) if int(w.q_lens[s]) * w.group > 32]
+    if dec and wide and not w.dense:
+        parts += [("decode_seqs", w.select(dec, f"{w.name}:decode_seqs")),
+                  ("wide_seqs", w.select(wide, f"{w.name}:wide_seqs"))]
+    off = {"softcap": dict(softcap=0.0), "alibi": dict(use_alibi=False, alibi_slopes=None),
+           "sinks": dict(use_sinks=False, sinks=None), "window": dict(window=0)}
+    on = {"softcap": w.softcap > 0, "alibi": w.use_alibi, "sinks": w.use_sinks,
+          "window": w.window > 0}
+    for feat, kw in off.items():
+        if on[feat]:
+            parts.append((f"no_{feat}", dataclasses.replace(w, name=f"{w.name}:no_{feat}", **kw)))
+    return parts
+
+
+def time_parts(args, extra_flags):
+    """One JSON line with the time of each part of the workload (see
+    part_batches); every part is its own batch, planned on its own."""
+    from varlen_attention_serving_amd import workloads as W
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = W.named(args.workload)
+    rows = []
+    for label, pw in part_batches(w):
+        r = Runner(pw.name, args.force, args.segment_tiles, extra_flags, w=pw)
+        t = r.time(args.steps, args.warmup, 1)
+        f = r.figures(t)
+        rows.append({"part": label, "num_seqs": pw.num_seqs, "total_q": pw.total_q,
+                     "plan": {"path": r.plan.path, "class_split": bool(r.plan.class_split),
+                              "stream_k": bool(r.plan.stream_k), "waves": r.plan.waves,
+                              "segments": r.plan.num_segments},
+                     "attention_kernel_ms_median": round(float(np.median(t["attn"])), 5),
+                     "gpu_ms_per_step_events_median": round(float(np.median(t["whole"])), 5),
+                     "algorithmic_bytes": r.work["bytes"], "algorithmic_flops": r.work["flops"],
+                     "bound": r.bound, "achieved": round(f["achieved"], 3), "unit": f["unit"],
+                     "frac": round(f["frac"], 4)})
+        r.close()
+        print(f"[bench]   {label:12s} attn {rows[-1]['attention_kernel_ms_median']:.4f} ms  "
+              f"step {rows[-1]['gpu_ms_per_step_events_median']:.4f} ms", file=sys.stderr,
+              flush=True)
+    print(json.dumps({"workload": args.workload, "steps": args.steps, "warmup": args.warmup,
+                      "timing": "HIP events around every step, medians", "parts": rows}),
+          flush=True)
+
+
 def make_read_flush(torch, nbytes=1 << 30):
     """A cache flush that only reads: the sum of a `nbytes` buffer (larger
     than L2 plus the 256 MiB MALL) into one value, so no dirty lines are left
@@ -561,6 +613,10 @@ def main():
                     help="wall-time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--prefill-cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the prefill figure's oracle baseline (0 = skip)")
+    ap.add_argument("--parts", action="store_true",
+                    help="instead of the bench line, time the parts of the workload: the "
+                         "whole batch, its decode-shaped and its wide sequences alone, and the "
+                         "batch with each optional feature (softcap, ALiBi, sinks, window) off")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (5 launches): the "
                          "reference dispatch for scaling HBM traffic counters")
@@ -609,9 +665,12 @@ def main():
             ap.error(f"unknown extras {sorted(unknown)}")
 
     from varlen_attention_serving_amd import binding as B
-    r = Runner(args.workload, args.force, args.segment_tiles,
-               (B.UA_FLAG_BF16_PARTIALS if args.bf16_partials else 0) |
-               (B.UA_FLAG_PERSISTENT if args.persistent else 0))
+    extra_flags = ((B.UA_FLAG_BF16_PARTIALS if args.bf16_partials else 0) |
+                   (B.UA_FLAG_PERSISTENT if args.persistent else 0))
+    if args.parts:
+        time_parts(args, extra_flags)
+        return
+    r = Runner(args.workload, args.force, args.segment_tiles, extra_flags)
     flush = make_read_flush(torch) if (args.cold or "cold" in extras) else None
     t = r.time(args.steps, args.warmup, args.event_every, flush if args.cold else None)
     f = r.figures(t)

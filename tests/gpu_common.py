@@ -10,6 +10,9 @@ from varlen_attention_serving_amd import device as D
 # acceptance bar: bf16/fp16 outputs against the fp64 oracle
 MAX_ABS = 2e-2
 REL_RMS = 5e-3
+# row LSE against the oracle's: the denominator sums 16-bit-rounded p, about
+# 2^-9 relative
+LSE_TOL = 4e-3
 
 
 def say(msg):

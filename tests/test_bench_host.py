@@ -89,3 +89,32 @@ def test_traffic_of_a_class_split_sums_its_timed_span(tmp_path, monkeypatch):
     read = (10 + 101 + 5) * 1024 * 2
     written = (8 + 3 + 1) * 1024
     assert t["bytes_per_launch"] == read + written
+
+
+def test_select_repacks_queries_and_keeps_the_pool():
+    from varlen_attention_serving_amd import workloads as W
+    w = W.random_small(11, num_seqs=5)
+    s = w.select([3, 0])
+    assert list(s.q_lens) == [w.q_lens[3], w.q_lens[0]]
+    assert list(s.seq_lens) == [w.seq_lens[3], w.seq_lens[0]]
+    assert list(s.cu_seqlens_q) == [0, w.q_lens[3], w.q_lens[3] + w.q_lens[0]]
+    lo3, hi3 = w.cu_seqlens_q[3], w.cu_seqlens_q[4]
+    assert (s.q[:hi3 - lo3] == w.q[lo3:hi3]).all()
+    assert (s.q[hi3 - lo3:] == w.q[:w.q_lens[0]]).all()
+    assert (s.block_table[0] == w.block_table[3]).all()
+    assert s.k_cache is w.k_cache and s.v_cache is w.v_cache
+
+
+def test_parts_split_a_mixed_batch_and_switch_features_off():
+    from varlen_attention_serving_amd import workloads as W
+    w = W.named("chunked_prefill_mix")
+    parts = dict(bench.part_batches(w))
+    assert list(parts) == ["all", "decode_seqs", "wide_seqs", "no_softcap", "no_window"]
+    assert parts["decode_seqs"].num_seqs + parts["wide_seqs"].num_seqs == w.num_seqs
+    assert parts["decode_seqs"].total_q + parts["wide_seqs"].total_q == w.total_q
+    # bytes split between the two classes: the second batch adds one cu_seqlens_q entry
+    total = bench.algorithmic_work(w)["bytes"]
+    assert (bench.algorithmic_work(parts["decode_seqs"])["bytes"]
+            + bench.algorithmic_work(parts["wide_seqs"])["bytes"]) == total + 4
+    assert parts["no_softcap"].softcap == 0.0 and parts["no_window"].window == 0
+    assert dict(bench.part_batches(W.named("long_prefill"))).keys() == {"all"}

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import compare, compare_rows, full_rows, run_hip, say
+from gpu_common import LSE_TOL, compare, compare_rows, full_rows, run_hip, say
 from varlen_attention_serving_amd import binding as B
 from varlen_attention_serving_amd import device as D
 from varlen_attention_serving_amd import workloads as W
@@ -325,7 +325,6 @@ def test_dense_layout(i):
     assert np.array_equal(o, paged)
 
 
-LSE_TOL = 4e-3  # the denominator sums 16-bit-rounded p: about 2^-9 relative
 
 LSE_CASES = [
     # (name, workload maker, force)

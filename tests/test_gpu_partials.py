@@ -14,14 +14,13 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import compare, run_hip, say
+from gpu_common import LSE_TOL, compare, run_hip, say
 from varlen_attention_serving_amd import binding as B
 from varlen_attention_serving_amd import device as D
 from varlen_attention_serving_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = 4e-3
 
 
 @pytest.fixture(scope="module", autouse=True)

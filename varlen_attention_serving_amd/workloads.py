@@ -105,6 +105,22 @@ class Workload:
         """Sequence index of each packed query token."""
         return np.repeat(np.arange(self.num_seqs, dtype=np.int64), self.q_lens)
 
+    def select(self, seqs, name: Optional[str] = None) -> "Workload":
+        """The batch of sequences ``seqs`` alone (same cache pool, same values;
+        queries repacked in the given order).  Paged layouts only."""
+        if self.dense:
+            raise ValueError("select() needs a paged workload")
+        idx = np.asarray(seqs, dtype=np.int64)
+        ql = self.q_lens[idx].astype(np.int32)
+        cu = np.zeros(len(idx) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(ql)
+        parts = [self.q[self.cu_seqlens_q[s]:self.cu_seqlens_q[s + 1]] for s in idx]
+        q = np.concatenate(parts) if parts else self.q[:0]
+        return dataclasses.replace(
+            self, name=name or f"{self.name}[{len(idx)} seqs]", q_lens=ql,
+            seq_lens=self.seq_lens[idx].astype(np.int32), cu_seqlens_q=cu,
+            block_table=self.block_table[idx].copy(), q=q)
+
 
 # ----------------------------------------------------------------------------
 # storage-type rounding (input preparation only)
