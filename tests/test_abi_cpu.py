@@ -411,3 +411,12 @@ def test_merge_rejects_a_missing_set_and_partial_mode_needs_lse():
         assert "partial_lse" in B.ua_last_error()
     finally:
         B.ua_destroy_problem(h)
+
+
+def test_ceiling_probe_library_loads_and_exports_its_probes():
+    """The test-only ceiling probes (built by __graft_entry__.build) load on a
+    host without a GPU; nothing is launched."""
+    import ceilings
+    L = ceilings.lib()
+    for name in ("uac_stream_read", "uac_paged_read", "uac_issue_rate"):
+        assert hasattr(L, name), name
