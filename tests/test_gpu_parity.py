@@ -342,6 +342,16 @@ LSE_CASES = [
         "lse_sk32", 903, np.ones(30, np.int64), np.random.default_rng(903).integers(1, 900, 30),
         num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, window=200,
         use_sinks=True), "auto"),
+    # softcap alone: its tile max is taken over 1 / (1 + e^{2y}) and folded
+    # into the exponent; the LSE checks that bookkeeping exactly
+    ("2d_ring_softcap_window", lambda: W.random_small(905, num_seqs=5, max_q=90, max_k=400,
+                                                      num_q_heads=16, num_kv_heads=4,
+                                                      head_dim=128, block_size=32, softcap=12.0,
+                                                      window=150), "2d"),
+    ("stream_k_32rows_softcap_sinks", lambda: W.build(
+        "lse_sk32_cap", 906, np.ones(30, np.int64), np.random.default_rng(906).integers(1, 1500, 30),
+        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, softcap=25.0,
+        use_sinks=True), "auto"),
     ("stream_k_16rows_fp8_d256", lambda: W.build(
         "lse_sk16", 904, np.ones(30, np.int64), np.random.default_rng(904).integers(1, 900, 30),
         num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=32, kv_dtype=W.DT_FP8_E4M3,

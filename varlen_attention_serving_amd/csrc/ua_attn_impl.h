@@ -116,12 +116,13 @@ constexpr int kSkMaxHeads = UA_SK_HEADS;
 static_assert(kSkMaxHeads <= kSkMaxWorkerWaves, "the workspace bound counts at most 8 waves a worker");
 
 // Score transforms a kernel is compiled for: none (the scale folds into the
-// exponent), softcap and/or ALiBi (tested per tile from the flags), or those
-// plus the QQ-bias, whose per-element loads cost registers the others need not
-// pay for.
+// exponent), softcap and/or ALiBi (tested per tile from the flags), those plus
+// the QQ-bias, whose per-element loads cost registers the others need not pay
+// for, or softcap alone (its last step folds into the exponent).
 constexpr int kXfNone = 0;
 constexpr int kXfScore = 1;
 constexpr int kXfQQ = 2;
+constexpr int kXfCap = 3;
 // log2-unit slack before the running reference max is moved (p <= 2^8)
 constexpr float kLazyRescale = 8.0f;
 
@@ -187,6 +188,16 @@ __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     float m;
     asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(r[0]), "v"(r[1]));
+    return m;
+}
+
+// min(x of lane l, x of lane l ^ 32) in every lane, as max_halves (values
+// are finite or +inf, never NaN).
+__device__ __forceinline__ float min_halves(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    float m;
+    asm("v_min_f32 %0, %1, %2" : "=v"(m) : "v"(r[0]), "v"(r[1]));
     return m;
 }
 
@@ -674,33 +685,66 @@ __device__ __forceinline__ void softmax_max(const UaKernelParams& p, f32x16 (&sa
     // into the exponent as one FMA: 2^(x c - m).
     const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
     float mt = -INFINITY;
-    if (XF != 0) {
-        // QQ-bias only on tiles that reach the query section (ctx is the same
-        // for every row of a q-block, so the test is uniform)
-        const bool qq = XF == kXfQQ && key0 + BN > rc.ctx;
-        transform_scores<NKT, 16>(
-            p, sacc,
-            [&](int kt, int i) { return key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3); }, rc,
-            qq);
-    }
-    if (need_mask) {
+    if constexpr (XF == kXfCap) {
+        // Softcap alone: the score in log2 units is C tanh(y) = C - 2C r with
+        // r = 1 / (1 + e^{2y}) and C = c log2(e), a decreasing function of r.
+        // Keep r in place of the score (masked keys: r = +inf), take the tile
+        // max as C - 2C min(r) (-inf when every key is masked), and let
+        // softmax_exp form the exponent (C - m) - 2C r in one FMA.
+        float rt = INFINITY;
+        // the masked and the plain tile in separate loops under one uniform
+        // test, so plain tiles carry no per-key compares
+        if (need_mask) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool keep = (key >= rc.kmin) & (key <= rc.kmax);
-                const float sv = keep ? sacc[kt][i] : -INFINITY;
-                sacc[kt][i] = sv;
-                mt = fmaxf(mt, sv);
-            }
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool keep = (key >= rc.kmin) & (key <= rc.kmax);
+                    const float r =
+                        __builtin_amdgcn_rcpf(1.0f + fast_exp2(sacc[kt][i] * p.softcap_in2));
+                    sacc[kt][i] = keep ? r : INFINITY;
+                    rt = fminf(rt, sacc[kt][i]);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    sacc[kt][i] = __builtin_amdgcn_rcpf(1.0f + fast_exp2(sacc[kt][i] * p.softcap_in2));
+                    rt = fminf(rt, sacc[kt][i]);
+                }
+        }
+        mt = __builtin_fmaf(-2.0f * p.softcap_out, min_halves(rt), p.softcap_out);
     } else {
+        if (XF != 0) {
+            // QQ-bias only on tiles that reach the query section (ctx is the same
+            // for every row of a q-block, so the test is uniform)
+            const bool qq = XF == kXfQQ && key0 + BN > rc.ctx;
+            transform_scores<NKT, 16>(
+                p, sacc,
+                [&](int kt, int i) { return key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3); }, rc,
+                qq);
+        }
+        if (need_mask) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+                    const bool keep = (key >= rc.kmin) & (key <= rc.kmax);
+                    const float sv = keep ? sacc[kt][i] : -INFINITY;
+                    sacc[kt][i] = sv;
+                    mt = fmaxf(mt, sv);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
+        }
+        mt = max_halves(mt) * c;
     }
-    mt = max_halves(mt) * c;
     // Lazy reference max: exponents are taken against m_run, which moves only
     // when some row's tile max exceeds it by more than kLazyRescale (log2
     // units).  Softmax is shift-invariant, so o and l stay exact relative to
@@ -723,13 +767,15 @@ __device__ __forceinline__ void softmax_exp(const UaKernelParams& p, const f32x1
                                             float m_run, float& l_run,
                                             typename QType<QT>::v8 (&pf)[BN / 16]) {
     typedef QType<QT> Q;
-    const float c = XF != 0 ? 1.0f : p.qk_scale_log2;
+    // softcap alone: sacc holds r, the exponent is (C - m) - 2C r (softmax_max)
+    const float c = XF == kXfCap ? -2.0f * p.softcap_out : XF != 0 ? 1.0f : p.qk_scale_log2;
+    const float b = XF == kXfCap ? p.softcap_out - m_run : -m_run;
 #pragma unroll
     for (int kc = 0; kc < BN / 16; ++kc) {
         const int kt = kc >> 1, q8 = (kc & 1) * 8;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            pf[kc][j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, -m_run));
+            pf[kc][j] = (QT)fast_exp2(__builtin_fmaf(sacc[kt][q8 + j], c, b));
         // the denominator sums the same rounded p the PV product uses
 #pragma unroll
         for (int j = 0; j < 8; j += 2) l_run = Q::sum2(pf[kc][j], pf[kc][j + 1], l_run);
@@ -2189,6 +2235,11 @@ hipError_t launch_geometry(const UaKernelParams& p, const UaLaunch& l, hipStream
 template <int D, typename QT, bool FP8>
 hipError_t launch_xform(const UaKernelParams& p, const UaLaunch& l, hipStream_t st) {
     if (p.flags & UA_FLAG_QQ_BIAS) return launch_geometry<D, QT, FP8, kXfQQ>(p, l, st);
+    // softcap alone folds into the exponent where the registers allow (at
+    // d = 256 the register path would spill)
+    if constexpr (D <= 128)
+        if ((p.flags & UA_FLAG_SOFTCAP) && !(p.flags & UA_FLAG_ALIBI))
+            return launch_geometry<D, QT, FP8, kXfCap>(p, l, st);
     if (p.flags & (UA_FLAG_SOFTCAP | UA_FLAG_ALIBI))
         return launch_geometry<D, QT, FP8, kXfScore>(p, l, st);
     return launch_geometry<D, QT, FP8, kXfNone>(p, l, st);
