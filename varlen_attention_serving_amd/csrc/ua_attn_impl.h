@@ -657,17 +657,21 @@ __device__ __forceinline__ void qk_tile(const unsigned short* __restrict__ k_lds
         sacc[kt] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) sacc[kt] = Q::mma(a[kc], qf[kc], sacc[kt]);
-        if constexpr (SWZ && D <= 128) {
-            // On the ring, keep four fragment reads ahead of the MFMA chain
-            // (then one read per MFMA): the default schedule kept two, and
-            // each MFMA waited on its read (measured about +0.6-3% on prefill).
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+        if constexpr (SWZ) {
+            // On the ring, keep AH fragment reads ahead of the MFMA chain
+            // (then one read per MFMA): the default schedule kept fewer, and
+            // each MFMA waited on its read.  AH = 4 at d <= 128 (about
+            // +0.6-3% on prefill); at d = 256, where the O and Q registers
+            // leave less room, AH = 2 (d = 256 prefill 0.731 -> 0.708 ms;
+            // AH = 4 spilled 12 registers).
+            constexpr int AH = D <= 128 ? 4 : 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // DS reads
 #pragma unroll
-            for (int i = 0; i < D / 16 - 4; ++i) {
+            for (int i = 0; i < D / 16 - AH; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
         }
     }
 }
