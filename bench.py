@@ -588,7 +588,7 @@ def main():
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "chunked_prefill_mix", "long_prefill",
                              "variant_mix", "tiny_varlen", "dense_prefill", "mha_prefill",
-                             "d256_prefill"])
+                             "d256_prefill", "decode_large"])
     ap.add_argument("--force", choices=["auto", "2d", "3d"], default="auto")
     ap.add_argument("--cold", action="store_true",
                     help="time the main workload cold: a read-only 1 GiB flush before every "

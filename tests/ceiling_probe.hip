@@ -24,6 +24,14 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// one 16-byte load, plain or non-temporal (the nt hint: streamed once, do not keep)
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ src, int64_t n_vec,
                                                    uint32_t* __restrict__ out) {
     // each wave reads 8 consecutive 1 KB runs per pass (8 loads in flight per
@@ -37,12 +45,12 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ src
     for (; base + U * 64 <= n_vec; base += n_waves * U * 64) {
         u32x4 v[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = src[base + j * 64 + lane];
+        for (int j = 0; j < U; ++j) v[j] = load16<NT>(src + base + j * 64 + lane);
 #pragma unroll
         for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
     }
     for (int64_t i = base + lane; i < n_vec && i < base + U * 64; i += 64) {
-        const u32x4 a = src[i];
+        const u32x4 a = load16<NT>(src + i);
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
@@ -63,6 +71,7 @@ struct PagedArgs {
 };
 
 // d = 128, 16-bit K/V: a key row of one head is 256 bytes (16 chunks of 16)
+template <bool NT>
 __global__ __launch_bounds__(512) void paged_read(PagedArgs a) {
     const int lane = threadIdx.x & 63;
     const int head = threadIdx.x >> 6;
@@ -83,8 +92,8 @@ __global__ __launch_bounds__(512) void paged_read(PagedArgs a) {
             const int64_t slot = ((int64_t)bt[key >> a.block_size_log2] << a.block_size_log2) +
                                  (key & ((1 << a.block_size_log2) - 1));
             const int64_t off = slot * slot_bytes + (int64_t)head * 256 + chunk * 16;
-            kv[i] = *reinterpret_cast<const u32x4*>(a.k + off);
-            kv[8 + i] = *reinterpret_cast<const u32x4*>(a.v + off);
+            kv[i] = load16<NT>(reinterpret_cast<const u32x4*>(a.k + off));
+            kv[8 + i] = load16<NT>(reinterpret_cast<const u32x4*>(a.v + off));
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc ^= kv[i].x ^ kv[i].y ^ kv[i].z ^ kv[i].w;
@@ -135,26 +144,30 @@ __global__ __launch_bounds__(64) void issue_rate(int iters, uint64_t* cycles, ui
 }  // namespace
 
 // Read n_bytes (a multiple of 16) of src with `blocks` workgroups of 256
-// threads; out holds blocks * 256 words.  Returns 0 or the HIP error.
-extern "C" int uac_stream_read(const void* src, int64_t n_bytes, int blocks, void* out, void* stream) {
+// threads (nt: non-temporal loads); out holds blocks * 256 words.  Returns 0
+// or the HIP error.
+extern "C" int uac_stream_read(const void* src, int64_t n_bytes, int blocks, int nt, void* out,
+                               void* stream) {
     if (n_bytes % 16 || blocks < 1) return -1;
-    hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4*>(src), n_bytes / 16, static_cast<uint32_t*>(out));
+    hipLaunchKernelGGL(nt ? stream_read<true> : stream_read<false>, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), n_bytes / 16,
+                       static_cast<uint32_t*>(out));
     return (int)hipGetLastError();
 }
 
-// The decode-shaped paged read: `workers` workgroups of num_kv_heads waves;
-// out holds workers * 64 * num_kv_heads words.  d = 128, 16-bit K/V.
+// The decode-shaped paged read: `workers` workgroups of num_kv_heads waves
+// (nt: non-temporal loads); out holds workers * 64 * num_kv_heads words.
+// d = 128, 16-bit K/V.
 extern "C" int uac_paged_read(const void* k, const void* v, const int32_t* block_table,
                               const int32_t* seq_lens, const int32_t* tile_seq,
                               const int32_t* tile_idx, int64_t n_tiles, int bt_stride,
-                              int block_size_log2, int num_kv_heads, int workers, void* out,
-                              void* stream) {
+                              int block_size_log2, int num_kv_heads, int workers, int nt,
+                              void* out, void* stream) {
     if (num_kv_heads < 1 || num_kv_heads > 8 || workers < 1 || n_tiles < 0) return -1;
     PagedArgs a{static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v),
                 block_table, seq_lens, tile_seq, tile_idx, n_tiles, bt_stride, block_size_log2,
                 num_kv_heads, static_cast<uint32_t*>(out)};
-    hipLaunchKernelGGL(paged_read, dim3(workers), dim3(64 * num_kv_heads), 0,
+    hipLaunchKernelGGL(nt ? paged_read<true> : paged_read<false>, dim3(workers), dim3(64 * num_kv_heads), 0,
                        static_cast<hipStream_t>(stream), a);
     return (int)hipGetLastError();
 }

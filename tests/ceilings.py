@@ -46,9 +46,9 @@ def lib():
         L = ctypes.CDLL(LIB)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.uac_stream_read.restype = i32
-        L.uac_stream_read.argtypes = [vp, i64, i32, vp, vp]
+        L.uac_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
         L.uac_paged_read.restype = i32
-        L.uac_paged_read.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
+        L.uac_paged_read.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp]
         L.uac_issue_rate.restype = i32
         L.uac_issue_rate.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         _lib = L
@@ -72,8 +72,9 @@ def _time(fn, reps, warmup=3):
     return float(np.median(ts))
 
 
-def stream_read(nbytes=4 << 30, blocks_per_cu=8, reps=20):
-    """Read-only streaming bandwidth (GB/s) over an `nbytes` buffer."""
+def stream_read(nbytes=4 << 30, blocks_per_cu=8, reps=20, nt=False):
+    """Read-only streaming bandwidth (GB/s) over an `nbytes` buffer (nt:
+    non-temporal loads)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks = cus * blocks_per_cu
@@ -83,17 +84,17 @@ def stream_read(nbytes=4 << 30, blocks_per_cu=8, reps=20):
     L = lib()
 
     def run():
-        rc = L.uac_stream_read(src.data_ptr(), nbytes, blocks, out.data_ptr(), s)
+        rc = L.uac_stream_read(src.data_ptr(), nbytes, blocks, int(nt), out.data_ptr(), s)
         assert rc == 0, rc
     ms = _time(run, reps)
     return {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "ms": round(ms, 4),
             "workgroups": blocks}
 
 
-def paged_read(seed=2, reps=20, block_size=16, num_kv_heads=8, workers_per_cu=1):
+def paged_read(seed=2, reps=20, block_size=16, num_kv_heads=8, workers_per_cu=1, nt=False):
     """The decode batch's K/V traffic alone: 64 sequences of S_k ~ U{512..8192}
     (the decode batch's lengths), 16-key blocks in random order, 8 kv heads,
-    d = 128, 16-bit; GB/s of K+V bytes visited."""
+    d = 128, 16-bit; GB/s of K+V bytes visited (nt: non-temporal loads)."""
     import torch
     from varlen_attention_serving_amd import workloads as W
     sp = W.named_spec("decode_batch")
@@ -126,7 +127,7 @@ def paged_read(seed=2, reps=20, block_size=16, num_kv_heads=8, workers_per_cu=1)
     def run():
         rc = L.uac_paged_read(k.data_ptr(), v.data_ptr(), table.data_ptr(), sl.data_ptr(),
                               tile_seq.data_ptr(), tile_idx.data_ptr(), n_tiles, bt_stride, lb,
-                              num_kv_heads, workers, out.data_ptr(), s)
+                              num_kv_heads, workers, int(nt), out.data_ptr(), s)
         assert rc == 0, rc
     ms = _time(run, reps)
     kv_bytes = int(seq_lens.sum()) * num_kv_heads * 128 * 2 * 2

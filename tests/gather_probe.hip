@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64) void probe_loader16(ProbeArgs a) {
     const int64_t slot_bytes = a.kv_slot_stride * G::ESZ;
     const unsigned char* base_k = reinterpret_cast<const unsigned char*>(a.k) + (int64_t)hk * D * G::ESZ;
     const unsigned char* base_v = reinterpret_cast<const unsigned char*>(a.v) + (int64_t)hk * D * G::ESZ;
-    Loader16<D, QT, FP8, BIG> ld;
+    Loader16<D, QT, FP8, BIG, true> ld;  // as the 16-row engine instantiates it
     ld.init(lane);
     ld.ids(a.block_table + (int64_t)s * a.bt_stride, t, s_k, lb, lane);
     ld.load(base_k, base_v, t, s_k, lb, slot_bytes, lane);

@@ -217,10 +217,12 @@ def _named_plan(name, extra=0, split_segment_tiles=0):
 
 @pytest.mark.parametrize("name,path,split", [("tiny_varlen", 2, 0), ("decode_batch", 3, 0),
                                              ("chunked_prefill_mix", 2, 0),
-                                             ("long_prefill", 2, 0), ("variant_mix", 2, 1)])
+                                             ("long_prefill", 2, 0), ("variant_mix", 2, 1),
+                                             ("decode_large", 3, 0)])
 def test_shape_rule(name, path, split):
-    """2D when the q-block x kv-head grid fills the device or a q-block visits
-    few keys (short context or a short window); otherwise the split path.
+    """2D when the q-block x kv-head grid of wide q-blocks fills the device or
+    a q-block visits few keys (short context or a short window); otherwise
+    the split path, and stream-K for decode-shaped batches of any size.
     Wide batches on the register-staged path (fp8 K/V, d = 256) send their
     decode-shaped sequences to a stream-K launch and keep the rest as one
     unsegmented 2D launch beside it; on the LDS ring a batch whose full grid
@@ -228,7 +230,7 @@ def test_shape_rule(name, path, split):
     plan, ws = _named_plan(name)
     assert plan.path == path
     assert plan.class_split == split
-    if name == "decode_batch":
+    if name in ("decode_batch", "decode_large"):
         assert plan.stream_k == 1 and plan.waves == 1 and plan.tile_n == 32
     if split:
         assert plan.waves == 4 and plan.stream_k == 1
@@ -301,50 +303,37 @@ def test_i64_addressing_reported_above_2gib():
 
 def test_shape_rule_scales_with_the_compute_units():
     """[UA] section 6 states the 2D threshold in workgroups per compute unit
-    (4 per CU): a part with half the CUs takes the 2D path for the decode
-    batch's 640-workgroup grid, the full MI355X (256 CUs, the default when
-    no device is queried) splits it."""
-    plan, _ = _named_plan("decode_batch")
-    assert plan.path == 3
-    h = B.ua_create_problem(_desc(num_q_heads=32, num_kv_heads=8, num_blocks=20000,
-                                  max_num_seqs=64, max_blocks_per_seq=512, max_total_q=64,
-                                  max_seqlen_k=8192, num_cus=128))
-    try:
-        assert B.ua_query_plan(h, 64, 64, 1, 8138).path == 2
-    finally:
-        B.ua_destroy_problem(h)
-    h = B.ua_create_problem(_desc(num_q_heads=32, num_kv_heads=8, num_blocks=20000,
-                                  max_num_seqs=64, max_blocks_per_seq=512, max_total_q=64,
-                                  max_seqlen_k=8192, num_cus=256))
-    try:
-        assert B.ua_query_plan(h, 64, 64, 1, 8138).path == 3
-    finally:
-        B.ua_destroy_problem(h)
+    (4 per CU): one 2528-query prefill chunk of 8192 keys at H_k = 8 has a
+    640-workgroup 2D grid, which a part with half the CUs takes as it is,
+    while the full MI355X (256 CUs, the default when no device is queried)
+    cuts it into segments to fill its round."""
+    kw = dict(num_q_heads=32, num_kv_heads=8, num_blocks=20000, max_num_seqs=64,
+              max_blocks_per_seq=512, max_total_q=4096, max_seqlen_k=8192)
+    for cus, path in ((128, 2), (256, 3), (0, 3)):
+        h = B.ua_create_problem(_desc(num_cus=cus, **kw))
+        try:
+            plan = B.ua_query_plan(h, 1, 2528, 2528, 8192)
+            assert plan.path == path and plan.stream_k == 0 and plan.waves == 4, (cus, plan.path)
+        finally:
+            B.ua_destroy_problem(h)
     with pytest.raises(B.UaError) as e:
         B.ua_create_problem(_desc(num_cus=-1))
     assert "num_cus" in B.ua_last_error()
 
 
-def test_no_alloc_refuses_before_touching_a_device():
-    """ua_run_no_alloc takes no workspace and refuses a batch whose split
-    partials exceed its scratch; both checks come before any device call."""
-    d = _desc(flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_FORCE_3D, split_segment_tiles=1,
-              max_total_q=600_000)
-    h = B.ua_create_problem(d)
+def test_decode_batches_stream_at_any_size():
+    """Decode-shaped batches (every q-block one wave) take the stream-K
+    split whatever their count once their keys are not short; at or below
+    512 keys a q-block has few tiles and the 2D path keeps them."""
+    h = B.ua_create_problem(_desc(num_q_heads=32, num_kv_heads=8, num_blocks=80000,
+                                  max_num_seqs=1024, max_blocks_per_seq=512, max_total_q=1024,
+                                  max_seqlen_k=8192))
     try:
-        args = B.ua_run_args_t(q=16, k_cache=16, v_cache=16, o=16 * 3, block_table=16,
-                               seq_lens=16, cu_seqlens_q=16, num_seqs=4, max_seqlen_q=60,
-                               total_q=600_000, max_seqlen_k=1000, block_table_stride=63,
-                               q_stride_tok=8 * 128, o_stride_tok=8 * 128)
-        with pytest.raises(B.UaError) as e:
-            B.ua_run_no_alloc(h, args, None)
-        assert e.value.status == B.UA_ERR_WORKSPACE
-        assert "scratch" in B.ua_last_error()
-        args.workspace = 256
-        args.workspace_bytes = 1 << 20
-        with pytest.raises(B.UaError) as e:
-            B.ua_run_no_alloc(h, args, None)
-        assert e.value.status == B.UA_ERR_INVALID_ARG
+        for n, sk in ((64, 8138), (128, 8192), (512, 8192), (1024, 4096)):
+            plan = B.ua_query_plan(h, n, n, 1, sk)
+            assert (plan.path, plan.stream_k, plan.waves) == (3, 1, 1), (n, sk)
+        plan = B.ua_query_plan(h, 512, 512, 1, 500)
+        assert (plan.path, plan.stream_k) == (2, 0)
     finally:
         B.ua_destroy_problem(h)
 

@@ -578,7 +578,7 @@ def test_gqa_groups_decode_batch(i, force):
 
 @pytest.mark.parametrize("name", ["decode_batch", "chunked_prefill_mix", "long_prefill",
                                   "variant_mix", "dense_prefill", "mha_prefill",
-                                  "d256_prefill"])
+                                  "d256_prefill", "decode_large"])
 def test_named_workload_full_size(name):
     """The benchmark's launch configuration at full size.  O starts as NaN and
     must come back finite everywhere (run_hip); every (token, head) row of the

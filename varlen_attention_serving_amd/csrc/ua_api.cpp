@@ -167,8 +167,10 @@ ua_status_t segmented(const ua_problem& P, int cus, int64_t total_q, int64_t liv
     return UA_OK;
 }
 
+// sk_cap: bytes the stream-K partials may take (the caller's workspace, or
+// the no-alloc scratch)
 ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t total_q,
-                      int32_t max_q, int32_t max_k, Plan* out) {
+                      int32_t max_q, int32_t max_k, size_t sk_cap, Plan* out) {
     const ua_problem_desc_t& d = P.d;
     Plan pl{};
     pl.small_block_q = use_rows16(P) ? 16 / P.group : P.group <= 32 ? 32 / P.group : 0;
@@ -193,7 +195,17 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
     if (w.slots > INT32_MAX / 2) return fail(UA_ERR_UNSUPPORTED, "too many query blocks");
     // q-blocks that carry rows (at most one partial block per sequence)
     const int64_t live_blocks = std::min<int64_t>(w.slots, num_seqs + total_q / w.block_q);
-    bool two_d = (int64_t)d.num_kv_heads * w.slots >= (int64_t)4 * cus || span <= 512;
+    // Decode-shaped batches stream on the stream-K workers whatever their
+    // size once a q-block's keys are not short: section 6's grid threshold
+    // would send a batch of 128 or more decode rows (at H_k = 8) to the 2D
+    // path, where each single-wave q-block walks its own sequence and the
+    // ragged lengths leave a tail (measured at d = 128: 128 rows 0.522 ->
+    // 0.347 ms, 256 rows 0.890 -> 0.677 ms, 512 rows of 256-4096 keys 0.860 ->
+    // 0.730 ms; d = 64: 0.300 -> 0.191 ms).  A batch whose stream-K slots do
+    // not fit sk_cap keeps the 2D path, which needs no workspace.
+    const bool sk_room = stream_k_bytes(P, num_seqs, 32, kSkMaxWorkerWaves) <= sk_cap;
+    bool two_d = span <= 512 || (small ? !(sk_fits && sk_room)
+                                       : (int64_t)d.num_kv_heads * w.slots >= (int64_t)4 * cus);
     if (!small && !two_d) {
         // Wide q-blocks carry 128 fp32 rows of partials per segment, so split
         // them only when the query-tile grid is short of one resident round
@@ -410,7 +422,7 @@ ua_status_t ua_query_plan(ua_problem_t p, int32_t num_seqs, int64_t total_q, int
         return fail(UA_ERR_INVALID_ARG, "shape outside the problem's maxima");
     Plan pl;
     ua_status_t st = make_plan(*p, plan_cus(*p, false), num_seqs, total_q, max_seqlen_q,
-                               max_seqlen_k, &pl);
+                               max_seqlen_k, p->ws_bytes, &pl);
     if (st != UA_OK) return st;
     const Sub& g = pl.sub[pl.n - 1];  // the launch holding the widest rows
     info->path = g.path;
@@ -527,7 +539,7 @@ ua_status_t run_impl(ua_problem_t p, const ua_run_args_t* a, void* stream, bool 
 
     Plan pl;
     ua_status_t st = make_plan(*p, plan_cus(*p, true), a->num_seqs, a->total_q, a->max_seqlen_q,
-                               a->max_seqlen_k, &pl);
+                               a->max_seqlen_k, no_alloc ? kScratchBytes : p->ws_bytes, &pl);
     if (st != UA_OK) return st;
 
     UaKernelParams base{};

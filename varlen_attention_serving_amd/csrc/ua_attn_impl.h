@@ -288,7 +288,17 @@ struct TileGeom {
 // so its p is exactly 0).  The loaded words go to their registers untouched:
 // any use at load time (a select, say) would make each load wait for its data
 // and serialise the tile's gather.
-template <int D, int NW, int BN, typename QT, bool FP8>
+// One K/V load of type T: plain, or with the non-temporal hint (NT) for
+// gathers that read each byte once (the decode engines): a load-only probe of
+// the decode batch's paged reads moves 6.8 TB/s with the hint against 6.0
+// without it.
+template <bool NT, typename T>
+__device__ __forceinline__ T load_kv(const unsigned char* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+    return *reinterpret_cast<const T*>(p);
+}
+
+template <int D, int NW, int BN, typename QT, bool FP8, bool NT = false>
 struct KvLoader {
     typedef TileGeom<D, NW, BN, FP8> G;
     u32x4 kreg[G::NCH], vreg[G::NCH];
@@ -316,8 +326,8 @@ struct KvLoader {
             const int key = t * BN + row0 + i * G::RSTEP;
             const int kc = min(key, s_k - 1);
             const int64_t off = (((int64_t)phys[i] << lb) + (kc & bmask)) * slot_bytes + col;
-            kreg[i] = *reinterpret_cast<const u32x4*>(base_k + off);
-            vreg[i] = *reinterpret_cast<const u32x4*>(base_v + off);
+            kreg[i] = load_kv<NT, u32x4>(base_k + off);
+            vreg[i] = load_kv<NT, u32x4>(base_v + off);
         }
     }
     __device__ __forceinline__ void store(unsigned short* k_lds, unsigned short* v_lds) const {
@@ -1490,7 +1500,7 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
         return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
     };
 
-    KvLoader<D, 1, BN, QT, FP8> ld;
+    KvLoader<D, 1, BN, QT, FP8, true> ld;  // each key row is read once: non-temporal
     ld.init(lane);
     const Frag fr = padded_frag<D>(lane);
     ld.ids(bt_row(pc), pc.t, pc.s_k, lb);
@@ -1592,7 +1602,7 @@ struct Geom16 {
 
 // BIG: blocks of at least 16 keys, so each 16-key half of a tile lies in one
 // block and the V rows take their half's block id (no per-row table reads).
-template <int D, typename QT, bool FP8, bool BIG>
+template <int D, typename QT, bool FP8, bool BIG, bool NT = false>
 struct Loader16 {
     typedef Geom16<D, FP8> G;
     typedef QType<QT> Q;
@@ -1635,7 +1645,11 @@ struct Loader16 {
                 (lane >> 4) * 8 * G::ESZ;
 #pragma unroll
             for (int kc = 0; kc < G::NKC; ++kc) {
-                kreg[kb][kc] = *reinterpret_cast<const kword*>(row + 32 * G::ESZ * kc);
+                // K: plain loads.  With the non-temporal hint the K operand
+                // loads (16 key rows x 4 chunks a wave) measured slower: 64-row
+                // bf16 decode at d = 256 0.362 -> 0.395 ms, fp8 variant_mix's
+                // decode rows 0.055 -> 0.073 ms; V's 16-byte row chunks gain
+                kreg[kb][kc] = load_kv<false, kword>(row + 32 * G::ESZ * kc);
             }
         }
         const int col = vcc * 16;
@@ -1646,7 +1660,7 @@ struct Loader16 {
             const int ph = BIG ? ((vrow0 + i * G::RSTEP) >= 16 ? kphys[1] : kphys[0])
                                : vphys[BIG ? 0 : i];
             const int64_t off = (((int64_t)ph << lb) + (kc2 & bmask)) * slot_bytes + col;
-            vreg[i] = *reinterpret_cast<const u32x4*>(base_v + off);  // untouched until stored
+            vreg[i] = load_kv<NT, u32x4>(base_v + off);  // untouched until stored
         }
     }
     // the K operand of (kb, kc) in the Q type
@@ -1690,8 +1704,8 @@ __host__ __device__ inline int v16_frag_offset(int lane) {
 }
 
 // S^T of one tile from the K operands in registers
-template <int D, typename QT, bool FP8, bool BIG>
-__device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG>& ld,
+template <int D, typename QT, bool FP8, bool BIG, bool NT>
+__device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG, NT>& ld,
                                           const typename QType<QT>::v8 (&qf)[D / 32],
                                           f32x4 (&sacc)[2]) {
 #pragma unroll
@@ -1815,7 +1829,7 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
         return q.kv_row * slot_bytes + (int64_t)head(q) * D * G::ESZ;
     };
 
-    Loader16<D, QT, FP8, BIG> ld;
+    Loader16<D, QT, FP8, BIG, true> ld;  // each key row is read once: non-temporal
     ld.init(lane);
     const int v_frag = v16_frag_offset<D>(lane);
     ld.ids(bt_row(pc), pc.t, pc.s_k, lb, lane);
@@ -1860,7 +1874,7 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
         // QK consumes this tile's K operands before the next loads reuse them
         f32x4 sacc[2];
-        qk_tile16<D, QT, FP8, BIG>(ld, qf, sacc);
+        qk_tile16(ld, qf, sacc);
         if (x + 1 < B) {
             ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);

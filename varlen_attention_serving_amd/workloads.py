@@ -366,6 +366,15 @@ def _spec_decode_batch(seed):
                 kw=dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16))
 
 
+def _spec_decode_large(seed):
+    """256 decode sequences, S_k ~ U{512..8192}, H_q=32, H_k=8, d=128, b=16, bf16,
+    causal: the decode batch's shape at a serving batch four times larger."""
+    rng = np.random.default_rng(seed)
+    sk = rng.integers(512, 8192, size=256, endpoint=True)
+    return dict(q_lens=np.ones(256, np.int32), seq_lens=sk, rng=rng,
+                kw=dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16))
+
+
 def _spec_chunked_prefill_mix(seed):
     """32 decode sequences (S_k ~ U{1024..8192}) then 4 chunks of 512 queries with
     ctx ~ U{2048..6144}; H_q=32, H_k=8, d=128, b=32, bf16, causal, softcap 50,
@@ -432,6 +441,7 @@ NAMED_SPECS = {
     "dense_prefill": (6, _spec_dense_prefill),
     "mha_prefill": (7, _spec_mha_prefill),
     "d256_prefill": (8, _spec_d256_prefill),
+    "decode_large": (9, _spec_decode_large),
 }
 
 
@@ -477,6 +487,7 @@ NAMED = {
     "dense_prefill": lambda seed=6: named("dense_prefill", seed),
     "mha_prefill": lambda seed=7: named("mha_prefill", seed),
     "d256_prefill": lambda seed=8: named("d256_prefill", seed),
+    "decode_large": lambda seed=9: named("decode_large", seed),
 }
 
 
