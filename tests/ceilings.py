@@ -1,7 +1,7 @@
 """Build and run the ceiling probes (tests/ceiling_probe.hip) and the library
-GEMM rate: what the MI355X delivers to a read-only stream, to the decode
-kernel's paged reads without its math, to a bf16 hipBLASLt GEMM, and the
-issue cost of v_exp_f32 against v_fma_f32.
+GEMM rate: what the MI355X delivers to a read-only stream and to the decode
+kernel's paged reads without its math (plain and non-temporal loads), to a
+bf16 hipBLASLt GEMM, and the issue cost of v_exp_f32 against v_fma_f32.
 
     python tests/ceilings.py        one JSON line of the figures (needs a GPU)
 """
@@ -178,8 +178,9 @@ def main():
         print("ceilings.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sys.path.insert(0, ROOT)
-    out = {"stream_read": stream_read(), "paged_read": paged_read(), "issue_rate": issue_rate(),
-           "gemm_bf16": gemm()}
+    out = {"stream_read": stream_read(), "stream_read_nt": stream_read(nt=True),
+           "paged_read": paged_read(), "paged_read_nt": paged_read(nt=True),
+           "issue_rate": issue_rate(), "gemm_bf16": gemm()}
     print(json.dumps(out), flush=True)
 
 

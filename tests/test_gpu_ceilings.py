@@ -20,11 +20,12 @@ def _gpu():
 
 
 def test_read_probes_stay_below_the_hbm_peak():
-    r = ceilings.stream_read(nbytes=1 << 30, reps=5)
-    p = ceilings.paged_read(reps=5)
-    say(f"[gpu] stream read {r}; paged read {p}")
-    for x in (r, p):
-        assert 500.0 < x["GB/s"] < 1.05 * ceilings.HBM_PEAK_GBS
+    for nt in (False, True):
+        r = ceilings.stream_read(nbytes=1 << 30, reps=5, nt=nt)
+        p = ceilings.paged_read(reps=5, nt=nt)
+        say(f"[gpu] non-temporal={nt}: stream read {r}; paged read {p}")
+        for x in (r, p):
+            assert 500.0 < x["GB/s"] < 1.05 * ceilings.HBM_PEAK_GBS
 
 
 def test_issue_rate_of_exp_and_fma():
