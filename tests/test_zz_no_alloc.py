@@ -71,6 +71,10 @@ CASES = [
     # order (tolerance, not bitwise)
     ("stream_k_capped_workers", lambda: _decode(11, 900, 32, 8, 128, 400), 300,
      B.UA_FLAG_FORCE_3D, 0, False),
+    # 1100 decode sequences: their stream-K slots (140 MiB) exceed the scratch,
+    # so ua_run_no_alloc plans the 2D path where ua_run streams them; the
+    # second call's 300 fit (tolerance: different plans)
+    ("decode_beyond_scratch_2d", lambda: _decode(13, 1100, 32, 8, 128, 700), 300, 0, 0, False),
 ]
 
 
