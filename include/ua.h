@@ -67,8 +67,8 @@ enum {
                                     ring runs on the persistent schedule of section
                                     8.2 of the unified page: one workgroup per resident
                                     slot drawing q-blocks, heaviest first, from eight
-                                    work queues (one per XCD, so a kv head's K/V stays
-                                    in one L2); results are bitwise those of the
+                                    work queues (one per XCD, so a kv head's work
+                                    runs on one XCD); results are bitwise those of the
                                     default grid.  Needs 256 bytes of workspace
                                     (included in ua_workspace_size); other launches
                                     keep the default grid. */

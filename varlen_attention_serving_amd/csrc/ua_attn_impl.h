@@ -1234,7 +1234,7 @@ __global__ __launch_bounds__(256, min_waves_per_simd(D, 4)) void ua_attn_lds_ker
 // queues by item mod kPersistQueues.  Workgroup j draws from queue
 // j mod kPersistQueues: the dispatcher deals a launch's workgroups to the
 // XCDs round robin, so with H_k = 8 each XCD serves one kv head, whose K/V
-// then stays in that XCD's L2, as in the default grid, while the queue
+// is then read through that XCD's L2, as in the default grid, while the queue
 // balances the ragged q-blocks dynamically (the item order is fixed, so
 // every q-block is computed exactly as in the default grid).
 template <int D, typename QT, int XF>
