@@ -252,7 +252,11 @@ typedef struct ua_plan_info {
     int32_t grid[3];         /* launch grid of the attention kernel */
     int32_t use_i64_kv;      /* 1 when the KV pool exceeds 2^31 bytes */
     int32_t stream_k;        /* 1 when single-wave (decode-shaped) rows take the split
-                                path with KV tiles balanced over resident workers */
+                                path with KV tiles balanced over resident workers
+                                (never for head_dim 256 with 16-bit K/V, the QQ bias
+                                and q-blocks of more than 16 rows: that kernel is
+                                not built, and such batches take the segmented split
+                                or the 2D path) */
     int32_t class_split;     /* 1 when a wide batch's decode-shaped sequences run in a
                                 stream-K launch and the rest in the launch described above */
 } ua_plan_info_t;

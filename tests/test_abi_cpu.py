@@ -274,6 +274,44 @@ def test_mixed_batch_policy(i):
         assert plan.stream_k == 1
 
 
+QQ_D256_PLANS = [
+    # (H_q, H_k, kv dtype, QQ, max_q, forced 3D (or a sequence count in place of
+    # the default 16), (path, stream_k, block_m) expected)
+    (16, 4, B.UA_DTYPE_BF16, True, 7, False, (3, 0, 32)),    # 28-row blocks: segmented split
+    (16, 4, B.UA_DTYPE_BF16, True, 7, True, (3, 0, 32)),     # forced: the segmented split
+    (16, 4, B.UA_DTYPE_F16, True, 7, True, (3, 0, 32)),
+    (16, 4, B.UA_DTYPE_BF16, False, 7, False, (3, 1, 32)),   # without the QQ bias it streams
+    (16, 4, B.UA_DTYPE_FP8_E4M3, True, 7, False, (3, 1, 32)),  # fp8 K/V: built
+    (16, 4, B.UA_DTYPE_BF16, True, 4, False, (3, 1, 16)),    # 16-row blocks: the 16-row engine
+    (32, 1, B.UA_DTYPE_BF16, True, 1, False, (3, 0, 32)),    # g = 32: 32-row blocks
+    (16, 4, B.UA_DTYPE_BF16, True, 7, 256, (2, 0, 32)),      # 256 sequences: the grid fills
+]
+
+
+@pytest.mark.parametrize("i", range(len(QQ_D256_PLANS)))
+def test_qq_bias_d256_keeps_off_the_unbuilt_engine(i):
+    """At d = 256 with 16-bit K/V and the QQ bias, q-blocks of more than 16
+    rows never take the 32-row stream-K engine (not built for that
+    configuration): the batch takes the segmented split, or the 2D path once
+    its grid fills the device; the other configurations keep the engine."""
+    hq, hk, kvdt, qq, max_q, f3, (path, sk, bm) = QQ_D256_PLANS[i]
+    n = 16
+    if f3 not in (True, False):
+        n, f3 = f3, False
+    q_dtype = B.UA_DTYPE_F16 if kvdt == B.UA_DTYPE_F16 else B.UA_DTYPE_BF16
+    flags = B.UA_FLAG_CAUSAL | (B.UA_FLAG_QQ_BIAS if qq else 0) | (B.UA_FLAG_FORCE_3D if f3 else 0)
+    h = B.ua_create_problem(_desc(num_q_heads=hq, num_kv_heads=hk, head_dim=256, block_size=16,
+                                  q_dtype=q_dtype, kv_dtype=kvdt, flags=flags, num_blocks=4096,
+                                  max_num_seqs=256, max_blocks_per_seq=256, max_total_q=2048,
+                                  max_seqlen_k=4096))
+    try:
+        plan = B.ua_query_plan(h, n, n * max_q, max_q, 4000)
+    finally:
+        B.ua_destroy_problem(h)
+    assert (plan.path, plan.stream_k, plan.block_m) == (path, sk, bm)
+    assert plan.class_split == 0
+
+
 def test_segment_override_selects_the_segmented_split():
     plan, _ = _named_plan("decode_batch", split_segment_tiles=16)
     assert plan.path == 3 and plan.stream_k == 0 and plan.tiles_per_segment == 16

@@ -293,6 +293,33 @@ def test_qq_bias(i):
     _full_check(w, force, f"qq/{name}/{force}")
 
 
+QQ_D256_CASES = [
+    # (name, q dtype, kv dtype, force, stream-K expected)
+    ("bf16_auto", W.DT_BF16, W.DT_BF16, "auto", 0),
+    ("bf16_forced_3d", W.DT_BF16, W.DT_BF16, "3d", 0),
+    ("f16_forced_3d", W.DT_F16, W.DT_F16, "3d", 0),
+    ("fp8_forced_3d", W.DT_BF16, W.DT_FP8_E4M3, "3d", 1),
+]
+
+
+@pytest.mark.parametrize("i", range(len(QQ_D256_CASES)))
+def test_qq_bias_d256_28_row_blocks(i):
+    """QQ-bias at d = 256 on decode-shaped q-blocks of 17-32 rows (short
+    chunks of up to 7 positions at g = 4).  With 16-bit K/V the 32-row
+    stream-K kernel of this configuration is not built (the compiler dropped
+    a register copy of a spilled Q fragment, so every row's scores were
+    wrong): the plan takes the segmented split; fp8 K/V keeps the stream-K
+    engine."""
+    name, qdt, kvdt, force, sk = QQ_D256_CASES[i]
+    w = W.build(f"qq_d256_{name}", 970 + i, [7, 3, 7, 1, 5], [438, 300, 1200, 90, 777],
+                num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=16, q_dtype=qdt,
+                kv_dtype=kvdt, use_qq_bias=True, rng=np.random.default_rng(970 + i))
+    _, plan = _full_check(w, force, f"qq_d256/{name}/{force}")
+    assert plan.path == 3 and plan.stream_k == sk
+    if sk:
+        assert plan.block_m == 32
+
+
 DENSE_CASES = [
     # (name, shape (H_q, H_k, d, paged b), workload flags, force, max_q)
     ("2d_ring", (8, 2, 128, 16), dict(), "2d", 300),

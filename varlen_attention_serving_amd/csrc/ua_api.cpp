@@ -120,6 +120,15 @@ void geometry(const ua_problem& P, int waves, Sub* g) {
 // SIMD (measured: at d <= 128 the 32-row engine streams faster).
 bool use_rows16(const ua_problem& P) { return P.d.head_dim == 256 && P.group <= 16; }
 
+// The 32-row stream-K engine is not built for d = 256 with 16-bit K/V and the
+// QQ bias: in that instantiation the compiler (hipcc, ROCm 7.2) spills part of
+// a Q fragment and then feeds the MFMA a stale register in its place (a copy
+// it makes is never read), so its scores are wrong.  Such batches take the
+// segmented split or the 2D path instead.
+bool sk32_built(const ua_problem& P) {
+    return !(P.d.head_dim == 256 && !P.fp8 && (P.d.flags & UA_FLAG_QQ_BIAS));
+}
+
 void rows16(const ua_problem& P, Sub* g) {
     g->rows16 = 1;
     g->tile_n = kSkTile;
@@ -188,6 +197,9 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
     const bool small = (int64_t)std::max(max_q, 1) * P.group <= 32;
     const int64_t sk_tiles = (int64_t)num_seqs * d.num_kv_heads * (cdiv(std::max<int64_t>(span, 1), kSkTile) + 2);
     const bool sk_fits = sk_tiles < INT32_MAX;
+    // the stream-K engine a decode-shaped batch would take is built
+    const bool sk16 = use_rows16(P) && (int64_t)std::max(max_q, 1) * P.group <= 16;
+    const bool sk_ok = sk_fits && (sk16 || sk32_built(P));
 
     Sub& w = pl.sub[0];
     geometry(P, small ? 1 : 4, &w);
@@ -203,9 +215,11 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
     // 0.347 ms, 256 rows 0.890 -> 0.677 ms, 512 rows of 256-4096 keys 0.860 ->
     // 0.730 ms; d = 64: 0.300 -> 0.191 ms).  A batch whose stream-K slots do
     // not fit sk_cap keeps the 2D path, which needs no workspace.
+    // Decode-shaped batches without a built stream-K engine follow the wide
+    // rule: 2D once the grid fills the device, else the segmented split.
     const bool sk_room = stream_k_bytes(P, num_seqs, 32, kSkMaxWorkerWaves) <= sk_cap;
-    bool two_d = span <= 512 || (small ? !(sk_fits && sk_room)
-                                       : (int64_t)d.num_kv_heads * w.slots >= (int64_t)4 * cus);
+    const bool grid_full = (int64_t)d.num_kv_heads * w.slots >= (int64_t)4 * cus;
+    bool two_d = span <= 512 || (small && sk_ok ? !sk_room : grid_full);
     if (!small && !two_d) {
         // Wide q-blocks carry 128 fp32 rows of partials per segment, so split
         // them only when the query-tile grid is short of one resident round
@@ -237,7 +251,8 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
     // not, split 0.353 ms against 0.385 in one launch).  A d <= 128 ring batch
     // keeps one launch (the split measured slower there).
     const bool split = !small && !ring_fills && (!ring || d.head_dim > 128) && !force2 &&
-                       !force3 && pl.small_block_q > 0 && sk_fits && d.split_segment_tiles == 0;
+                       !force3 && pl.small_block_q > 0 && sk_fits && d.split_segment_tiles == 0 &&
+                       (use_rows16(P) || sk32_built(P));
     w.class_mode = split ? 2 : 0;
     // Beside a concurrent stream-K launch the wide q-blocks need no segments
     // to fill the device (measured: variant_mix 0.148 -> 0.125 ms unsplit).
@@ -270,9 +285,9 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
         g.grid[0] = d.num_kv_heads;
         g.grid[1] = (unsigned)g.slots;
         g.grid[2] = 1;
-    } else if (small && d.split_segment_tiles == 0 && sk_fits) {
+    } else if (small && d.split_segment_tiles == 0 && sk_ok) {
         // every sequence's rows fit one q-block: balance KV tiles over workers
-        if (use_rows16(P) && (int64_t)std::max(max_q, 1) * P.group <= 16) rows16(P, &g);
+        if (sk16) rows16(P, &g);
         g.path = 3;
         g.stream_k = 1;
         g.grid[0] = 0;  // resident worker count, fixed at launch

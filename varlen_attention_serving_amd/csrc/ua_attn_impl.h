@@ -2160,6 +2160,11 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
                 } else {
                     return hipErrorInvalidValue;
                 }
+            } else if constexpr (D == 256 && !FP8 && XF == kXfQQ) {
+                // not built: the compiler miscompiles this instantiation (it
+                // drops a register copy of a spilled Q fragment); the plan
+                // never asks for it
+                return hipErrorInvalidValue;
             } else {
                 // workers of sk_heads waves, one kv head each
                 int gh = sk_max_heads<D>();
