@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void probe_loader16(ProbeArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int kc = 0; kc < G::NKC; ++kc) {
-            const v8 x = ld.kop(kb, kc);
+            const v8 x = ld.template kop<0>(kb, kc);
             const int64_t row = (int64_t)i * G::BN + 16 * kb + (lane & 15);
             *reinterpret_cast<u32x4*>(&a.out_k[row * D + 32 * kc + 8 * (lane >> 4)]) =
                 __builtin_bit_cast(u32x4, x);

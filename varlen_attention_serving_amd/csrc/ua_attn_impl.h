@@ -1607,9 +1607,13 @@ struct Loader16 {
     typedef Geom16<D, FP8> G;
     typedef QType<QT> Q;
     typedef typename Q::v8 v8;
-    // K operands of the next tile: [kb][kc], 16 bytes (8 for fp8) per lane
+    // K operands: [buffer][kb][kc], 16 bytes (8 for fp8) per lane.  fp8 K
+    // with blocks of 16 keys or more takes two buffers, so the next tile's K
+    // is in flight while this one's is in use (32 registers); 16-bit K, and
+    // smaller blocks with their per-row V block ids, have room for one.
     typedef typename std::conditional<FP8, u32x2, u32x4>::type kword;
-    kword kreg[2][G::NKC];
+    static constexpr int KBUF = FP8 && BIG ? 2 : 1;
+    kword kreg[KBUF][2][G::NKC];
     u32x4 vreg[G::NCH];
     int kphys[2], vphys[BIG ? 1 : G::NCH];
     int vcc, vrow0;
@@ -1636,6 +1640,12 @@ struct Loader16 {
     // S_k read slot S_k - 1 and are masked (p = 0)
     __device__ __forceinline__ void load(const unsigned char* base_k, const unsigned char* base_v,
                                          int t, int s_k, int lb, int64_t slot_bytes, int lane) {
+        load_k<0>(base_k, t, s_k, lb, slot_bytes, lane);
+        load_v(base_v, t, s_k, lb, slot_bytes);
+    }
+    template <int BUF>
+    __device__ __forceinline__ void load_k(const unsigned char* base_k, int t, int s_k, int lb,
+                                           int64_t slot_bytes, int lane) {
         const int bmask = (1 << lb) - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -1649,9 +1659,13 @@ struct Loader16 {
                 // loads (16 key rows x 4 chunks a wave) measured slower: 64-row
                 // bf16 decode at d = 256 0.362 -> 0.395 ms, fp8 variant_mix's
                 // decode rows 0.055 -> 0.073 ms; V's 16-byte row chunks gain
-                kreg[kb][kc] = load_kv<false, kword>(row + 32 * G::ESZ * kc);
+                kreg[BUF][kb][kc] = load_kv<false, kword>(row + 32 * G::ESZ * kc);
             }
         }
+    }
+    __device__ __forceinline__ void load_v(const unsigned char* base_v, int t, int s_k, int lb,
+                                           int64_t slot_bytes) {
+        const int bmask = (1 << lb) - 1;
         const int col = vcc * 16;
 #pragma unroll
         for (int i = 0; i < G::NCH; ++i) {
@@ -1664,13 +1678,14 @@ struct Loader16 {
         }
     }
     // the K operand of (kb, kc) in the Q type
+    template <int BUF>
     __device__ __forceinline__ v8 kop(int kb, int kc) const {
         if constexpr (FP8) {
-            const u32x2 lo = Q::cvt_fp8x4(kreg[kb][kc][0]);
-            const u32x2 hi = Q::cvt_fp8x4(kreg[kb][kc][1]);
+            const u32x2 lo = Q::cvt_fp8x4(kreg[BUF][kb][kc][0]);
+            const u32x2 hi = Q::cvt_fp8x4(kreg[BUF][kb][kc][1]);
             return __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
         } else {
-            return __builtin_bit_cast(v8, kreg[kb][kc]);
+            return __builtin_bit_cast(v8, kreg[BUF][kb][kc]);
         }
     }
     __device__ __forceinline__ void store_v(unsigned short* v_lds) const {
@@ -1703,8 +1718,8 @@ __host__ __device__ inline int v16_frag_offset(int lane) {
     return (4 * G + J) * (D + kVPad16) + 4 * A;
 }
 
-// S^T of one tile from the K operands in registers
-template <int D, typename QT, bool FP8, bool BIG, bool NT>
+// S^T of one tile from the K operands in registers (buffer BUF)
+template <int BUF, int D, typename QT, bool FP8, bool BIG, bool NT>
 __device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG, NT>& ld,
                                           const typename QType<QT>::v8 (&qf)[D / 32],
                                           f32x4 (&sacc)[2]) {
@@ -1713,7 +1728,7 @@ __device__ __forceinline__ void qk_tile16(const Loader16<D, QT, FP8, BIG, NT>& l
         sacc[kb] = f32x4{};
 #pragma unroll
         for (int kc = 0; kc < D / 32; ++kc)
-            sacc[kb] = QType<QT>::mma16(ld.kop(kb, kc), qf[kc], sacc[kb]);
+            sacc[kb] = QType<QT>::mma16(ld.template kop<BUF>(kb, kc), qf[kc], sacc[kb]);
     }
 }
 
@@ -1865,18 +1880,31 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
     // needs no barrier, and fp8 workers run free (a barrier there cost 1%,
     // and 4% on variant_mix).
     constexpr bool WG_SYNC = !FP8;
-    for (int64_t x = A; x < B; ++x) {
+    constexpr int KBUF = Loader16<D, QT, FP8, BIG, true>::KBUF;
+    // One tile; its K operands sit in buffer BUF.  The next tile's V is
+    // loaded as soon as this tile's has left the registers, and its K into
+    // the other buffer before this tile's QK (two K buffers), else once QK
+    // has consumed this tile's operands.
+    auto step = [&](auto buf_c, int64_t x) {
+        constexpr int BUF = decltype(buf_c)::value;
+        constexpr int NXT = (BUF + 1) % KBUF;
         // this tile's V into LDS (the previous tile's reads are done: one
-        // wave, LDS operations in order), then the next tile's loads
+        // wave, LDS operations in order)
         if (WG_SYNC) __syncthreads();
         ld.store_v(v_lds);
+        if (x + 1 < B) {
+            ld.load_v(vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes);
+            if (KBUF == 2) {
+                ld.template load_k<NXT>(kc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
+                if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);
+            }
+        }
         const int key0 = pc.t * BN;
         const bool need_mask = !(key0 >= kr.full_lo && key0 + BN - 1 <= kr.full_hi);
-        // QK consumes this tile's K operands before the next loads reuse them
         f32x4 sacc[2];
-        qk_tile16(ld, qf, sacc);
-        if (x + 1 < B) {
-            ld.load(kc + hoff(p1), vc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
+        qk_tile16<BUF>(ld, qf, sacc);
+        if (KBUF == 1 && x + 1 < B) {
+            ld.template load_k<NXT>(kc + hoff(p1), p1.t, p1.s_k, lb, slot_bytes, lane);
             if (x + 2 < B) ld.ids(bt_row(p2), p2.t, p2.s_k, lb, lane);
         }
         softmax_pv16<D, QT, FP8, XF>(p, sacc, v_lds, oacc, m_run, l_run, key0, need_mask, ri.rc,
@@ -1901,6 +1929,14 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
         pc = p1;
         p1 = p2;
         if (x + 3 < B) p2 = sk_next<BN>(p, p2);
+    };
+    if constexpr (KBUF == 2) {
+        for (int64_t x = A; x < B; x += 2) {
+            step(std::integral_constant<int, 0>{}, x);
+            if (x + 1 < B) step(std::integral_constant<int, 1>{}, x + 1);
+        }
+    } else {
+        for (int64_t x = A; x < B; ++x) step(std::integral_constant<int, 0>{}, x);
     }
 }
 
