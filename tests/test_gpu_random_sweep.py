@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import compare, run_hip, say
+from gpu_common import compare, compare_rows, full_rows, run_hip, say
 from varlen_attention_serving_amd import binding as B
 from varlen_attention_serving_amd import workloads as W
 
@@ -31,9 +31,11 @@ def _gpu():
     yield
 
 
-def draw(i):
-    """Workload, forced path and segment override of case i, and a label."""
-    rng = np.random.default_rng(90_000 + i)
+def draw(i, medium=False):
+    """Workload, forced path and segment override of case i, and a label.
+    Medium cases take longer sequences (up to 700 queries over 3000 keys) and
+    more decode rows, so chains span many tiles, segments and workers."""
+    rng = np.random.default_rng((95_000 if medium else 90_000) + i)
     d = int(rng.choice([64, 128, 256]))
     g = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
     hk = int(rng.choice([1, 2, 4]))
@@ -44,10 +46,11 @@ def draw(i):
     flags = dict(causal=bool(rng.random() < 0.8),
                  softcap=float(rng.choice([3.0, 20.0])) if rng.random() < 0.3 else 0.0,
                  use_alibi=bool(rng.random() < 0.3),
-                 window=int(rng.integers(1, 200)) if rng.random() < 0.3 else 0,
+                 window=int(rng.integers(1, 1500 if medium else 200)) if rng.random() < 0.3 else 0,
                  use_sinks=bool(rng.random() < 0.3),
                  use_qq_bias=bool(rng.random() < 0.1))
-    n_dec = int(rng.integers(0, 9))
+    max_ctx_dec, max_q, max_ctx = (3000, 700, 2300) if medium else (400, 91, 300)
+    n_dec = int(rng.integers(0, 33 if medium else 9))
     n_long = int(rng.integers(0, 4))
     if n_dec + n_long == 0:
         n_long = 1
@@ -55,11 +58,11 @@ def draw(i):
     for _ in range(n_dec):
         ql = int(rng.integers(1, 3))
         q_lens.append(ql)
-        seq_lens.append(ql + int(rng.integers(0, 400)))
+        seq_lens.append(ql + int(rng.integers(0, max_ctx_dec)))
     for _ in range(n_long):
-        ql = int(rng.integers(3, 91))
+        ql = int(rng.integers(3, max_q))
         q_lens.append(ql)
-        seq_lens.append(ql + int(rng.integers(0, 300)))
+        seq_lens.append(ql + int(rng.integers(0, max_ctx)))
     if rng.random() < 0.15:
         pos = int(rng.integers(0, len(q_lens) + 1))
         q_lens.insert(pos, 0)
@@ -69,7 +72,7 @@ def draw(i):
     seq_lens = np.array(seq_lens, np.int64)[order]
     force = FORCES[int(rng.integers(0, len(FORCES)))]
     seg = 2 if force == "3d_seg" else 0
-    w = W.build(f"sweep{i}", 90_000 + i, q_lens, seq_lens, num_q_heads=g * hk, num_kv_heads=hk,
+    w = W.build(f"{'medium' if medium else 'sweep'}{i}", 90_000 + i, q_lens, seq_lens, num_q_heads=g * hk, num_kv_heads=hk,
                 head_dim=d, block_size=16 if dense else b, q_dtype=q_dtype, kv_dtype=kv_dtype,
                 rng=rng, **flags)
     if dense:
@@ -94,3 +97,24 @@ def test_random_configuration(i):
     if force in ("3d", "3d_seg"):
         assert plan.path == 3
     compare(o, oracle.attention(w), f"sweep {i}")
+
+
+N_MEDIUM = 24
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_random_medium_configuration(i):
+    """Longer random batches, compared on every decode row and, for the
+    longer sequences, on every token with the query head rotating through
+    its group (every q-block of every kv head visited)."""
+    w, force, seg, label = draw(i, medium=True)
+    say(f"[gpu] medium {label}")
+    o, plan = run_hip(w, FLAG[force], split_segment_tiles=seg)
+    say(f"  plan path={plan.path} split={plan.class_split} stream_k={plan.stream_k} "
+        f"waves={plan.waves} block_m={plan.block_m} segments={plan.num_segments}")
+    if force == "2d":
+        assert plan.path == 2
+    if force in ("3d", "3d_seg"):
+        assert plan.path == 3
+    rows, m = full_rows(w, budget_flops=2e10)
+    compare_rows(o, w, rows, f"medium {i} ({rows.size} rows, {m} kv heads per token)")
