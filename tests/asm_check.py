@@ -118,14 +118,55 @@ def compile_asm(out_dir):
         return list(ex.map(one, srcs))
 
 
-def check(out_dir=None):
-    """[(source, kernel, spill stores, dead writes)] over the library's kernels."""
-    rows = []
+_ENTRY = re.compile(r"^  - \.(\w+):\s*(\S*)")
+_FIELD = re.compile(r"^    \.(\w+):\s*(\S*)")
+
+
+def metadata(asm_path):
+    """{kernel: {vgpr_count, agpr_count, vgpr_spill_count, ...}} from the code
+    object metadata at the end of an assembly file (one list entry per
+    kernel; its argument descriptions are nested deeper and skipped)."""
+    out, entry, inside = {}, None, False
+
+    def close():
+        if entry and "name" in entry:
+            out[entry.pop("name")] = entry
+
+    with open(asm_path) as f:
+        for line in f:
+            if line.startswith("amdhsa.kernels:"):
+                inside = True
+                continue
+            if not inside:
+                continue
+            m = _ENTRY.match(line) or _FIELD.match(line)
+            if not m:
+                if line and not line.startswith(" "):
+                    break  # the end of the kernels list
+                continue
+            if line.startswith("  - "):
+                close()
+                entry = {}
+            key, val = m.group(1), m.group(2)
+            entry[key] = val if key == "name" else (int(val) if val.isdigit() else val)
+    close()
+    return out
+
+
+def check_with_metadata(out_dir=None):
+    """check()'s rows and every kernel's metadata, from one compile."""
+    rows, meta = [], {}
     with tempfile.TemporaryDirectory() as tmp:
         for path in compile_asm(out_dir or tmp):
             for fn, spills, dead in scan(path):
                 rows.append((os.path.basename(path), fn, spills, dead))
-    return rows
+            meta.update(metadata(path))
+    return rows, meta
+
+
+def check(out_dir=None):
+    """[(source, kernel, spill stores, dead writes)] over the library's kernels."""
+    return check_with_metadata(out_dir)[0]
 
 
 def main():

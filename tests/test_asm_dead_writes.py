@@ -1,7 +1,8 @@
 """No kernel of the library writes a vector register that it never reads (see
 tests/asm_check.py): the pattern of a miscompile found in one instantiation,
-which the library no longer builds.  Compiles the kernel sources to gfx950
-assembly on the CPU (about 45 s)."""
+which the library no longer builds.  From the same assembly, the register
+budgets the measured launch shapes rely on.  Compiles the kernel sources to
+gfx950 assembly on the CPU (about 45 s)."""
 import os
 
 import pytest
@@ -10,8 +11,21 @@ import asm_check
 
 
 @pytest.fixture(scope="module")
-def kernels():
-    return asm_check.check()
+def compiled():
+    return asm_check.check_with_metadata()
+
+
+@pytest.fixture(scope="module")
+def kernels(compiled):
+    return compiled[0]
+
+
+def _regs(meta, name):
+    """Registers a lane of the kernel holds (VGPRs and AGPRs share one file of
+    512), rounded up to the allocation granule of 8."""
+    m = meta[name]
+    n = m["vgpr_count"] + m.get("agpr_count", 0)
+    return -(-n // 8) * 8
 
 
 def test_every_kernel_reads_what_it_writes(kernels):
@@ -53,3 +67,32 @@ def test_the_scan_flags_a_dropped_copy(tmp_path):
     [(fn, spills, dead)] = list(asm_check.scan(str(asm)))
     assert fn == "_ZN2ua1kEv" and spills == 1
     assert set(dead) == {("v", 254)}
+
+
+# the kernels of the measured launch shapes (head dim, Q type, K/V type, score transforms)
+WIDE_FP8_D256 = "_ZN2ua14ua_attn_kernelILi256ELi4ELi32EDF16_Lb1ELb0ELi1EEEv14UaKernelParams"
+DECODE16_FP8_D256 = "_ZN2ua18ua_decode16_kernelILi256EDF16_Lb1ELi1ELb1EEEv14UaKernelParams"
+RING_D128 = "_ZN2ua18ua_attn_lds_kernelILi128EDF16bLb0ELi0EEEv14UaKernelParams"
+RING_D128_CAP = "_ZN2ua18ua_attn_lds_kernelILi128EDF16bLb0ELi3EEEv14UaKernelParams"
+DECODE_SK_D128 = "_ZN2ua19ua_decode_sk_kernelILi128ELi32EDF16bLb0ELi0EEEv14UaKernelParams"
+
+
+def test_class_split_kernels_fit_side_by_side(compiled):
+    """In a class split (the fp8 d = 256 mix: ALiBi, sinks, window) a CU that
+    holds a wide workgroup, one wave per SIMD, must still hold a 16-row
+    decode wave beside it on every SIMD, or the decode launch waits for the
+    wide one to drain."""
+    _, meta = compiled
+    assert _regs(meta, WIDE_FP8_D256) + _regs(meta, DECODE16_FP8_D256) <= 512
+
+
+def test_measured_kernels_budgets(compiled):
+    """Occupancy and spills of the kernels behind the measured workloads: the
+    d = 128 ring keeps three waves per SIMD (168 registers) and the 32-row
+    decode engine two (256), all without vector spills."""
+    _, meta = compiled
+    assert _regs(meta, RING_D128) <= 168 and meta[RING_D128]["vgpr_spill_count"] == 0
+    assert _regs(meta, RING_D128_CAP) <= 168
+    assert _regs(meta, DECODE_SK_D128) <= 256 and meta[DECODE_SK_D128]["vgpr_spill_count"] == 0
+    for k in (WIDE_FP8_D256, DECODE16_FP8_D256):
+        assert _regs(meta, k) <= 256 and meta[k]["vgpr_spill_count"] == 0, k
