@@ -245,16 +245,19 @@ RING_POLICY = [
     (32, 8, 128, 2, 0, 40, 1),                   # blocks below one copy's 4 rows
     (16, 8, 256, 32, 0, 96, 0),                  # d = 256 ring, grid fills a round
     (16, 2, 256, 32, 0, 64, 1),                  # d = 256 ring, grid too small
-    (16, 8, 256, 32, B.UA_FLAG_SOFTCAP, 96, 1),  # d = 256 with a transform
-    (16, 8, 256, 32, B.UA_FLAG_ALIBI, 96, 1),
+    (16, 8, 256, 32, B.UA_FLAG_SOFTCAP, 96, 0),  # d = 256 ring with softcap or ALiBi
+    (16, 8, 256, 32, B.UA_FLAG_ALIBI, 96, 0),
+    (16, 2, 256, 32, B.UA_FLAG_ALIBI, 64, 1),    # ... grid too small
+    (16, 8, 256, 32, B.UA_FLAG_QQ_BIAS, 96, 1),  # d = 256 with the QQ bias: register path
+    (16, 8, 256, 32, B.UA_FLAG_ALIBI | B.UA_FLAG_QQ_BIAS, 96, 1),
 ]
 
 
 @pytest.mark.parametrize("i", range(len(RING_POLICY)))
 def test_mixed_batch_policy(i):
     """Decode rows plus four 512-query chunks: LDS-ring batches (16-bit K/V,
-    blocks of at least 512 / d keys, at d = 256 only without softcap, ALiBi
-    or QQ-bias) stay one 2D launch when their full grid fills a resident
+    blocks of at least 512 / d keys, at d = 256 not with the QQ bias) stay
+    one 2D launch when their full grid fills a resident
     round; other wide batches, and d = 256 ring batches that do not fill it,
     send the decode rows to the concurrent stream-K launch.  A d <= 128 ring
     batch never splits."""

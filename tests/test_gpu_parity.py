@@ -207,22 +207,52 @@ def test_mixed_decode_and_chunks(i):
     assert plan.class_split == want_split
 
 
-def test_d256_ring_batch_in_one_launch():
-    """A d = 256 16-bit batch without score transforms whose full grid fills a
-    resident round stays one 2D launch on the two-stage LDS ring, decode
-    q-blocks and chunks together."""
-    rng = np.random.default_rng(420)
+D256_RING_FLAGS = [dict(use_sinks=True, window=400),
+                   dict(use_alibi=True, use_sinks=True),
+                   dict(softcap=15.0, window=300),
+                   dict(softcap=30.0, use_alibi=True)]
+
+
+@pytest.mark.parametrize("i", range(len(D256_RING_FLAGS)))
+def test_d256_ring_batch_in_one_launch(i):
+    """A d = 256 16-bit batch (with or without softcap and ALiBi) whose full
+    grid fills a resident round stays one 2D launch on the two-stage LDS
+    ring, decode q-blocks and chunks together."""
+    rng = np.random.default_rng(420 + i)
     n_dec = 96
     dec_k = rng.integers(1, 500, size=n_dec, endpoint=True)
     ch_q = rng.integers(40, 120, size=4, endpoint=True)
     ctx = rng.integers(0, 300, size=4, endpoint=True)
     q_lens = np.concatenate([np.ones(n_dec, np.int64), ch_q])
     order = rng.permutation(q_lens.size)
-    w = W.build("d256_ring_mixed", 420, q_lens[order], np.concatenate([dec_k, ctx + ch_q])[order],
+    w = W.build(f"d256_ring_mixed{i}", 420 + i, q_lens[order], np.concatenate([dec_k, ctx + ch_q])[order],
                 num_q_heads=16, num_kv_heads=8, head_dim=256, block_size=16, rng=rng,
-                use_sinks=True, window=400)
+                **D256_RING_FLAGS[i])
     _, plan = _full_check(w, "auto")
     assert plan.path == 2 and plan.class_split == 0
+
+
+D256_RING_XF = [
+    # (name, shape (H_q, H_k, d, b), flags, force)
+    ("2d_alibi", (16, 4, 256, 16), dict(use_alibi=True), "2d"),
+    ("2d_softcap_f16_b64", (16, 4, 256, 64), dict(softcap=20.0, q_dtype=W.DT_F16, kv_dtype=W.DT_F16), "2d"),
+    ("2d_softcap_alibi_b2", (8, 2, 256, 2), dict(softcap=5.0, use_alibi=True, use_sinks=True), "2d"),
+    ("seg_softcap_alibi_noncausal", (16, 2, 256, 32), dict(softcap=30.0, use_alibi=True, causal=False),
+     "3d_seg"),
+    ("seg_alibi_window_sinks", (8, 2, 256, 16), dict(use_alibi=True, window=90, use_sinks=True), "3d_seg"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(D256_RING_XF)))
+def test_d256_ring_score_transforms(i):
+    """The two-stage d = 256 ring with softcap and ALiBi, in one launch and
+    on the segmented split: full tiles, the diagonal's masked tiles and each
+    sequence's partial last tile (ragged lengths), blocks from the smallest
+    the ring takes (2 keys) to 64."""
+    name, (hq, hk, d, b), flags, force = D256_RING_XF[i]
+    w = W.random_small(980 + i, num_seqs=5, max_q=150, max_k=420, num_q_heads=hq,
+                       num_kv_heads=hk, head_dim=d, block_size=b, **flags)
+    _full_check(w, force, f"d256_ring/{name}/{force}")
 
 
 @pytest.mark.parametrize("d,b", [(64, 1), (64, 4), (128, 2), (128, 4), (64, 8)])

@@ -227,13 +227,12 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
         const int64_t wide_grid = (int64_t)d.num_kv_heads * (total_q / w.block_q + 1);
         two_d = wide_grid >= (int64_t)kWideResidentPerCU * cus;
     }
-    // Wide q-blocks of 16-bit K/V run on the LDS ring (at d = 256 only
-    // without score transforms; blocks must hold one copy's 512 / d key
-    // rows), which streams a decode-shaped q-block's keys at HBM speed inside
-    // the same launch: keep the whole batch in one 2D launch once its full
-    // grid (every sequence's slots) fills a resident round.
-    const uint32_t score_xf = UA_FLAG_SOFTCAP | UA_FLAG_ALIBI | UA_FLAG_QQ_BIAS;
-    const bool ring = !P.fp8 && (d.head_dim <= 128 || !(d.flags & score_xf)) &&
+    // Wide q-blocks of 16-bit K/V run on the LDS ring (at d = 256 not with
+    // the QQ bias; blocks must hold one copy's 512 / d key rows), which
+    // streams a decode-shaped q-block's keys at HBM speed inside the same
+    // launch: keep the whole batch in one 2D launch once its full grid
+    // (every sequence's slots) fills a resident round.
+    const bool ring = !P.fp8 && (d.head_dim <= 128 || !(d.flags & UA_FLAG_QQ_BIAS)) &&
                       (int64_t(1) << P.log2_block) * d.head_dim >= 512 &&
                       (int64_t)d.num_kv_heads * d.head_dim * 2 * (512 / d.head_dim) < (int64_t(1) << 31);
     const bool ring_fills =
@@ -244,7 +243,7 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
 
     // Otherwise the decode-shaped sequences of a wide batch go to the
     // stream-K kernel, beside the wide launch that keeps the rest: for
-    // register-staged wide launches (fp8 K/V, d = 256 with score transforms,
+    // register-staged wide launches (fp8 K/V, d = 256 with the QQ bias,
     // blocks below one copy's rows) and for d = 256 ring batches too small
     // to fill a round (measured with 64 decode rows and 4 chunks of 512:
     // H_k = 8 fills it, one launch 0.70 ms against 0.75 split; H_k = 2 does

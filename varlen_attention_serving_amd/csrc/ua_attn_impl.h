@@ -2221,13 +2221,13 @@ hipError_t launch_attn(const UaKernelParams& p0, const UaLaunch& l, hipStream_t 
         }
     } else {
         // 16-bit K/V in four-wave workgroups take the LDS ring when one
-        // wave-wide copy's key rows always share a block.  At d = 256 only
-        // without score transforms: the swizzled tiles' lane addresses cost
-        // registers the padded ones do not, and with softcap or ALiBi the
-        // ring's variant spills (measured 1-4% slower than the register path
-        // on softcap prefill, against 7-11% faster without transforms).
+        // wave-wide copy's key rows always share a block.  At d = 256 not
+        // with the QQ bias, whose per-element loads the ring's registers
+        // cannot hold; with softcap or ALiBi the d = 256 ring spills, but only
+        // in its masked and partial-tile branches, and still beats the
+        // register path, which loads each tile after the barrier.
         constexpr bool ring_built = UA_LDS_RING && NW == 4 && BN == LdsGeom<D>::BN && !FP8 &&
-                                    D <= UA_LDS_RING_MAX_D && (D <= 128 || XF == kXfNone);
+                                    D <= UA_LDS_RING_MAX_D && (D <= 128 || XF != kXfQQ);
         const bool ring = ring_built && (1 << p.block_size_log2) >= LdsGeom<D>::ROWS_PER_OP &&
                           p.kv_slot_stride * 2 * LdsGeom<D>::ROWS_PER_OP < (int64_t(1) << 31);
         const bool split = l.path == 3;
