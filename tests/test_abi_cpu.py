@@ -277,6 +277,29 @@ def test_mixed_batch_policy(i):
         assert plan.stream_k == 1
 
 
+@pytest.mark.parametrize("q_lens,want", [((1024, 1024), 0), ((1024, 1024, 1), 1),
+                                          ((1024, 1024, 2), 1), ((1024, 1024, 3), 0)])
+def test_no_class_split_without_a_decode_shaped_sequence(q_lens, want):
+    """An fp8 d = 256 batch (H 16/2: the 16-row stream-K q-blocks hold two
+    query positions) splits off its decode-shaped sequences only when one can
+    exist: the shortest sequence holds at least total_q - (n - 1) * max_q
+    queries."""
+    sk_max = 4096
+    n, total, mx = len(q_lens), sum(q_lens), max(q_lens)
+    desc = _desc(num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=64, q_dtype=B.UA_DTYPE_F16,
+                 kv_dtype=B.UA_DTYPE_FP8_E4M3, flags=B.UA_FLAG_CAUSAL | B.UA_FLAG_ALIBI,
+                 num_blocks=n * sk_max // 64, max_num_seqs=n, max_blocks_per_seq=sk_max // 64,
+                 max_total_q=total, max_seqlen_k=sk_max)
+    h = B.ua_create_problem(desc)
+    try:
+        plan = B.ua_query_plan(h, n, total, mx, sk_max)
+    finally:
+        B.ua_destroy_problem(h)
+    assert plan.class_split == want
+    if not want:
+        assert plan.path == 3 and plan.stream_k == 0  # the wide rule: a segmented split
+
+
 QQ_D256_PLANS = [
     # (H_q, H_k, kv dtype, QQ, max_q, forced 3D (or a sequence count in place of
     # the default 16), (path, stream_k, block_m) expected)

@@ -249,9 +249,17 @@ ua_status_t make_plan(const ua_problem& P, int cus, int32_t num_seqs, int64_t to
     // H_k = 8 fills it, one launch 0.70 ms against 0.75 split; H_k = 2 does
     // not, split 0.353 ms against 0.385 in one launch).  A d <= 128 ring batch
     // keeps one launch (the split measured slower there).
+    // No split when no sequence can be decode-shaped: the shortest holds at
+    // least total_q - (num_seqs - 1) * max_q queries (a loose bound from the
+    // caller only costs the split, since the wide launch alone serves every
+    // sequence), and a stream-K launch with nothing to do still costs a
+    // launch and the wide q-blocks their segments (measured: two fp8 d = 256
+    // sequences of 1024 queries, 0.090 -> 0.080 ms a step).
+    const bool maybe_decode =
+        total_q - (int64_t)(num_seqs - 1) * std::max(max_q, 1) <= (int64_t)pl.small_block_q;
     const bool split = !small && !ring_fills && (!ring || d.head_dim > 128) && !force2 &&
-                       !force3 && pl.small_block_q > 0 && sk_fits && d.split_segment_tiles == 0 &&
-                       (use_rows16(P) || sk32_built(P));
+                       !force3 && pl.small_block_q > 0 && maybe_decode && sk_fits &&
+                       d.split_segment_tiles == 0 && (use_rows16(P) || sk32_built(P));
     w.class_mode = split ? 2 : 0;
     // Beside a concurrent stream-K launch the wide q-blocks need no segments
     // to fill the device (measured: variant_mix 0.148 -> 0.125 ms unsplit).
