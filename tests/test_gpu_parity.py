@@ -255,6 +255,31 @@ def test_d256_ring_score_transforms(i):
     _full_check(w, force, f"d256_ring/{name}/{force}")
 
 
+FP8_D256_WIDE = [
+    # (name, shape (H_q, H_k, d, b), flags, force): four-wave fp8 d = 256 tiles
+    ("2d_b4_alibi_sinks", (16, 2, 256, 4), dict(use_alibi=True, use_sinks=True), "2d"),
+    ("2d_b2_registers", (16, 2, 256, 2), dict(softcap=10.0), "2d"),
+    ("seg_b16_window_noncausal", (8, 2, 256, 16), dict(window=70, causal=False), "3d_seg"),
+    ("seg_b64_bf16q_softcap", (16, 4, 256, 64), dict(softcap=25.0, q_dtype=W.DT_BF16), "3d_seg"),
+    ("2d_b8_qq", (8, 2, 256, 8), dict(use_qq_bias=True), "2d"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FP8_D256_WIDE)))
+def test_fp8_d256_wide_tiles(i):
+    """fp8 K/V at d = 256 in four-wave q-blocks without a concurrent
+    stream-K launch (the register-staged gather converting each tile to the
+    Q type in LDS): the 2D path and the segmented split, every score
+    transform, blocks of 2 to 64 keys, ragged last tiles."""
+    name, (hq, hk, d, b), flags, force = FP8_D256_WIDE[i]
+    kw = dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3)
+    kw.update(flags)
+    w = W.random_small(1000 + i, num_seqs=5, max_q=150, max_k=420, num_q_heads=hq,
+                       num_kv_heads=hk, head_dim=d, block_size=b, **kw)
+    _, plan = _full_check(w, force, f"fp8_d256_wide/{name}/{force}")
+    assert plan.class_split == 0
+
+
 @pytest.mark.parametrize("d,b", [(64, 1), (64, 4), (128, 2), (128, 4), (64, 8)])
 def test_small_block_sizes(d, b):
     """Blocks smaller than the key rows one wave-wide LDS copy fills keep the
@@ -359,6 +384,8 @@ DENSE_CASES = [
      "2d", 90),
     ("d256_noncausal", (16, 4, 256, 32), dict(causal=False), "auto", 60),
     ("stream_k_decode", (32, 8, 128, 16), dict(use_sinks=True), "3d", 1),
+    ("2d_fp8_d256", (16, 4, 256, 32), dict(q_dtype=W.DT_F16, kv_dtype=W.DT_FP8_E4M3,
+                                                  use_alibi=True), "2d", 90),
     ("stream_k_16rows_d256_fp8", (16, 2, 256, 32), dict(kv_dtype=W.DT_FP8_E4M3, window=70),
      "auto", 1),
 ]
