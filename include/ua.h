@@ -318,8 +318,9 @@ ua_status_t ua_merge(const ua_merge_args_t* args, void* stream);
  * whose partials do not fit returns UA_ERR_WORKSPACE before anything is
  * enqueued (the stream-K workers are capped to the slots the scratch holds;
  * a segmented split must fit whole), except a decode-shaped batch whose
- * stream-K slots do not fit, which runs on the 2D path (no partials).  A class-split batch runs its two
- * launches one after the other on `stream` instead of forking a side stream.
+ * stream-K slots do not fit, which runs on the 2D path (no partials).  A
+ * class-split batch runs its two launches one after the other on `stream`
+ * instead of forking a side stream.
  * No part of the scratch needs to start at zero: every partial the reduce
  * reads is written earlier by the same call.  Calls on one GPU share its
  * scratch, so calls whose work overlaps on that GPU (other streams, other
