@@ -436,6 +436,15 @@ LSE_CASES = [
         "lse_sk32_cap", 906, np.ones(30, np.int64), np.random.default_rng(906).integers(1, 1500, 30),
         num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, softcap=25.0,
         use_sinks=True), "auto"),
+    # the d = 256 ring with softcap and ALiBi, one launch and segmented
+    ("2d_ring_d256_softcap_alibi", lambda: W.random_small(907, num_seqs=5, max_q=90, max_k=400,
+                                                          num_q_heads=16, num_kv_heads=4,
+                                                          head_dim=256, block_size=16, softcap=20.0,
+                                                          use_alibi=True, use_sinks=True), "2d"),
+    ("seg_ring_d256_alibi", lambda: W.random_small(908, num_seqs=5, max_q=90, max_k=400,
+                                                   num_q_heads=8, num_kv_heads=2, head_dim=256,
+                                                   block_size=32, use_alibi=True,
+                                                   use_sinks=True), "3d_seg"),
     ("stream_k_16rows_fp8_d256", lambda: W.build(
         "lse_sk16", 904, np.ones(30, np.int64), np.random.default_rng(904).integers(1, 900, 30),
         num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=32, kv_dtype=W.DT_FP8_E4M3,

@@ -136,6 +136,9 @@ SINGLE_CASES = [
      B.UA_FLAG_FORCE_3D, 0),
     ("class_split_fp8_d256", lambda: _mixed(23, 16, 2, 256, 64, kv_dtype=W.DT_FP8_E4M3,
                                             use_sinks=True, use_alibi=True, window=600), 0, 0),
+    ("2d_ring_d256_softcap_alibi", lambda: _mixed(24, 16, 4, 256, 32, use_sinks=True,
+                                                  use_alibi=True, softcap=30.0),
+     B.UA_FLAG_FORCE_2D, 0),
 ]
 
 
