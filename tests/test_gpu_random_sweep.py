@@ -18,7 +18,7 @@ from varlen_attention_serving_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 128
+N_CASES = 256
 FORCES = ("auto", "auto", "2d", "3d", "3d_seg")
 FLAG = {"auto": 0, "2d": B.UA_FLAG_FORCE_2D, "3d": B.UA_FLAG_FORCE_3D,
         "3d_seg": B.UA_FLAG_FORCE_3D}
@@ -99,7 +99,7 @@ def test_random_configuration(i):
     compare(o, oracle.attention(w), f"sweep {i}")
 
 
-N_MEDIUM = 24
+N_MEDIUM = 64
 
 
 @pytest.mark.parametrize("i", range(N_MEDIUM))
