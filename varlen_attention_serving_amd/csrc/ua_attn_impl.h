@@ -1461,13 +1461,14 @@ __global__ __launch_bounds__(64 * sk_max_heads<D>(), min_waves_per_simd(D, 1)) v
     typedef TileGeom<D, 1, BN, FP8> G;
     static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
 
-    // Decode waves take issue priority over other kernels' waves on their
-    // SIMDs: beside a concurrent wide launch (a class split) the decode
-    // launch is the longer one.  Measured on one box, interleaved, with both
-    // decode engines raised: variant_mix 0.1192 -> 0.1179 ms, and about 1%
-    // on decode batches alone too (decode_batch 0.1863 -> 0.1846 ms,
-    // decode_large 0.7136 -> 0.7068 ms).
-    __builtin_amdgcn_s_setprio(2);
+    // A decode launch of its own raises its waves' issue priority (measured
+    // on one box, interleaved: decode_batch 0.1863 -> 0.1846 ms, decode_large
+    // 0.7136 -> 0.7068 ms).  Beside a concurrent wide launch (a class split)
+    // it does not: the wide workgroups, starved, hold their compute units
+    // longer, and the decode workers queued behind them start later (the
+    // 128-row fp8 mix without its window 0.285 -> 0.337 ms, against 0.1192
+    // -> 0.1179 ms with it).
+    if (p.class_mode != 1) __builtin_amdgcn_s_setprio(2);
     // sk_heads waves, each with its own tiles (dynamic LDS sized at launch)
     extern __shared__ __attribute__((aligned(16))) unsigned short sk_lds[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1813,8 +1814,8 @@ __global__ __launch_bounds__(64 * sk16_max_heads(D, FP8), min_waves16(D, FP8)) v
     constexpr int BN = G::BN;
     static_assert(BN == kSkTile, "the reduce locates stream-K partials with this tile size");
 
-    // issue priority over other kernels' waves, as in ua_decode_sk_kernel
-    __builtin_amdgcn_s_setprio(2);
+    // issue priority when not beside a wide launch, as in ua_decode_sk_kernel
+    if (p.class_mode != 1) __builtin_amdgcn_s_setprio(2);
     // one V tile per wave (dynamic LDS sized at launch); the waves of a worker
     // share nothing else
     extern __shared__ __attribute__((aligned(16))) unsigned short sk16_lds[];
